@@ -1,0 +1,171 @@
+/*
+ * specverify — the target-side verify step of speculative sampling on MI355X (gfx950).
+ *
+ * C ABI.  Every array argument is a device pointer owned by the caller; the
+ * library allocates nothing, never synchronises, and enqueues its kernels on
+ * the caller's HIP stream.  Entry points are stateless and thread-safe; two
+ * calls that share a workspace must not overlap in time (put them on one
+ * stream, or give each its own workspace).
+ *
+ * Errors that the host can see from the arguments alone are returned as an
+ * sv_status before anything is launched.  Errors that depend on the data
+ * (a token out of range, a NaN logit, a bad temperature) cannot be seen
+ * without reading device memory; they are reported per sequence or per tree
+ * through the optional out_status array (SV_ROW_* bits) and the affected
+ * entries take a defined, in-range fallback result.
+ *
+ * Sources of the operations (cited by page title and section):
+ *  [SpS]  "論文解説: Speculative Sampling — ドラフトモデルによるLLMデコード高速化"
+ *         (0h-n0.github.io explainer of arXiv:2302.01318): Step 2 (ステップ2),
+ *         Step 3 (ステップ3) accept equation, modified rejection sampling
+ *         (修正付き棄却サンプリング) equation, expected speedup (期待される高速化),
+ *         the sequence diagram and the code sketch's speculative_decode
+ *         (gamma = look-ahead, temperature applied to both models).
+ *  [SpI]  SpecInfer article (abeam.tech, arXiv:2305.09781): basic idea
+ *         (基本アイデア) and inference (推論方法) — token-tree verification.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of the logits.  bf16 values are 16-bit brain-float patterns;
+ * both widen exactly to fp32 inside the kernels. */
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_NULL = 1,      /* a required pointer is NULL                                  */
+  SV_ERR_SHAPE = 2,     /* a size is out of range (see each entry point)               */
+  SV_ERR_DTYPE = 3,     /* dtype is not an sv_dtype                                    */
+  SV_ERR_WORKSPACE = 5, /* workspace is NULL or smaller than the *_workspace_bytes size */
+  SV_ERR_LAUNCH = 6     /* the HIP runtime refused a launch (hipGetLastError)          */
+} sv_status;
+
+/* Per-sequence / per-tree data-error bits written to out_status (0 = clean). */
+enum {
+  SV_ROW_TOKEN_RANGE = 1,     /* a draft token / tree node token is outside [0, V)            */
+  SV_ROW_NONFINITE = 2,       /* a logit row holds NaN or +inf, or only -inf (chain); NaN (tree) */
+  SV_ROW_RESIDUAL_ZERO = 4,   /* rejection with zero residual mass: drawn from p_k instead     */
+  SV_ROW_BAD_TREE = 8,        /* parents[0] != -1 or parents[i] not in [0, i)                  */
+  SV_ROW_BAD_TEMPERATURE = 16,/* temperature not finite and > 0                               */
+  SV_ROW_BAD_UNIFORM = 32     /* a uniform outside [0, 1)                                      */
+};
+
+/* Library version string, e.g. "specverify 0.1.0 gfx950". */
+const char* sv_version(void);
+
+/* Human-readable name of a status code (never NULL). */
+const char* sv_status_string(sv_status status);
+
+/* ------------------------------------------------------------------------------------------
+ * Chain verification ([SpS] Step 2, Step 3, modified rejection sampling).
+ *
+ * For each sequence b with temperature T = temperature[b]:
+ *   p_i = softmax(target_logits[b, i, :] / T)   i = 0..gamma   (row gamma = bonus position)
+ *   q_i = softmax(draft_logits[b, i, :] / T)    i = 0..gamma-1
+ *   draft token x_i = draft_tokens[b, i] is accepted while
+ *       uniforms[b, i] < min(1, p_i(x_i) / q_i(x_i))          (strict; q = 0 < p counts as +inf,
+ *                                                             p = q = 0 rejects)
+ *   k = number of leading accepts (the cut at the first rejection, [SpS] Step 3).
+ *   If k < gamma the replacement token is drawn from norm(max(0, p_k - q_k)); if that mass is
+ *   zero it is drawn from p_k and SV_ROW_RESIDUAL_ZERO is set.  If k == gamma a bonus token is
+ *   drawn from p_gamma.  Draws are by inverse CDF in token-id order with u = uniforms[b, gamma]:
+ *       y = min{ x : sum_{t<=x} w(t) > u * sum_t w(t) }.
+ *   out_tokens[b, :] = [x_0 .. x_{k-1}, y, -1 ...]; out_num_accepted[b] = k (k+1 tokens emitted).
+ *
+ * Arguments (all device pointers, caller-owned, contiguous row-major):
+ *   target_logits  [B, gamma+1, V] of dtype; target row i scores draft token i.
+ *   draft_logits   [B, gamma, V]   of dtype.
+ *   draft_tokens   int32 [B, gamma].
+ *   uniforms       fp32 [B, gamma+1]; columns 0..gamma-1 drive the accept tests, column gamma
+ *                  the draw.  The caller draws them (the library holds no random state).
+ *   temperature    fp32 [B].
+ *   B in [1, 2^24], gamma in [1, 64], V in [1, 2^31 - 1].
+ *   out_tokens        int32 [B, gamma+1]  (required)
+ *   out_num_accepted  int32 [B]           (required)
+ *   out_p, out_q      fp32 [B, gamma]: p_i(x_i), q_i(x_i) for every i < gamma (optional, NULL)
+ *   out_status        int32 [B]: SV_ROW_* bits (optional, NULL)
+ *   workspace         device scratch of at least sv_verify_chain_workspace_bytes(B, gamma, V,
+ *                     dtype) bytes, 256-byte aligned; no initialisation needed; contents are
+ *                     undefined after the call.
+ * Sequences with SV_ROW_TOKEN_RANGE, SV_ROW_NONFINITE, SV_ROW_BAD_TEMPERATURE or
+ * SV_ROW_BAD_UNIFORM take the fallback result k = 0, out_tokens = [0, -1, ...]; their out_p /
+ * out_q are unspecified.
+ * Any base pointer alignment is accepted; 16-byte-aligned logits with V a multiple of 4 (fp32)
+ * or 8 (bf16) take the vector-load path.
+ * ---------------------------------------------------------------------------------------- */
+size_t sv_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int64_t V, sv_dtype dtype);
+
+sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                          const int32_t* draft_tokens, const float* uniforms,
+                          const float* temperature, int32_t B, int32_t gamma, int64_t V,
+                          int32_t* out_tokens, int32_t* out_num_accepted, float* out_p,
+                          float* out_q, int32_t* out_status, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Greedy token-tree verification ([SpI] basic idea, inference).
+ *
+ * For each tree t: g[u] = argmax_x logits[t, u, x] for every node u (lowest x on ties, -0 == +0,
+ * NaN never the maximum).  Starting at the root u = 0, repeatedly move to the child c of u
+ * (lowest node id among children) with node_tokens[t, c] == g[u]; stop when there is none.
+ *   out_path[t, :]   = [0, c_1, .., c_k, -1 ...]          node ids of the accepted path
+ *   out_tokens[t, :] = [tok(c_1) .. tok(c_k), g[c_k], -1 ...]   accepted tokens + bonus argmax
+ *   out_num_accepted[t] = k
+ *
+ * Arguments (device pointers, caller-owned):
+ *   logits       [n_trees, n_nodes, V] of dtype; row u scores the children of node u.
+ *   parents      int32 [n_trees, n_nodes]; parents[t,0] = -1 and 0 <= parents[t,i] < i.
+ *   node_tokens  int32 [n_trees, n_nodes]; node 0 holds the last committed token (not emitted).
+ *   n_trees in [1, 2^24], n_nodes in [1, 4096], V in [1, 2^31 - 1].
+ *   out_path, out_tokens  int32 [n_trees, n_nodes] (required)
+ *   out_num_accepted      int32 [n_trees]          (required)
+ *   out_node_argmax       int32 [n_trees, n_nodes] g[u] (optional, NULL)
+ *   out_status            int32 [n_trees] SV_ROW_* bits (optional, NULL)
+ *   workspace             at least sv_verify_tree_workspace_bytes(...) bytes, 256-byte aligned.
+ * A tree with SV_ROW_BAD_TREE or SV_ROW_TOKEN_RANGE takes the fallback result: path [0],
+ * tokens [g[0]], k = 0.  NaN logits set SV_ROW_NONFINITE; NaN entries are skipped by the argmax
+ * (a row of only NaN gives 0) and the walk proceeds.
+ * ---------------------------------------------------------------------------------------- */
+size_t sv_verify_tree_workspace_bytes(int32_t n_trees, int32_t n_nodes, int64_t V,
+                                      sv_dtype dtype);
+
+sv_status sv_verify_tree(const void* logits, sv_dtype dtype, const int32_t* parents,
+                         const int32_t* node_tokens, int32_t n_trees, int32_t n_nodes, int64_t V,
+                         int32_t* out_path, int32_t* out_tokens, int32_t* out_num_accepted,
+                         int32_t* out_node_argmax, int32_t* out_status, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Kernel timing (measurement support; not part of the verify step).
+ *
+ * sv_trace_start(capacity): from now on, each kernel the library launches (up to `capacity`
+ *   launches in total) is bracketed by two HIP events recorded on its launch stream.  Creates
+ *   2*capacity HIP events (host-side objects; no device memory).  Returns 0, or -1 if event
+ *   creation failed.  Calling it again discards earlier records.
+ * sv_trace_stop(): stops recording; returns the number of launches recorded.
+ * sv_trace_kernels(): stops recording, waits for the recorded events, groups the launches by
+ *   kernel name and returns the number of distinct names (-1 on a HIP error).
+ * sv_trace_get(i, ...): name, launch count and total / min / max event-to-event milliseconds
+ *   of the i-th name from the last sv_trace_kernels(); returns 0, or -1 for a bad index.
+ * Not thread-safe with respect to concurrent verify calls on other threads.
+ * ---------------------------------------------------------------------------------------- */
+int sv_trace_start(int capacity);
+int sv_trace_stop(void);
+int sv_trace_kernels(void);
+int sv_trace_get(int index, char* name, size_t name_len, int* launches, double* total_ms,
+                 double* min_ms, double* max_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

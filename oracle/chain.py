@@ -129,7 +129,7 @@ def inverse_cdf(w, u):
 def _fallback(gamma, status):
     return {
         "k": 0, "tokens": [0], "p_at": np.full(gamma, np.nan), "q_at": np.full(gamma, np.nan),
-        "status": status, "flag_accept": [], "edge": 1.0, "draw": None,
+        "status": status, "flag_accept": [], "edge": 1.0, "draw": None, "weights": None,
     }
 
 
@@ -145,7 +145,8 @@ def verify_chain_seq(target, draft, draft_tokens, uniforms, temperature, force=N
     Returns a dict: k (drafts accepted), tokens (the k accepted drafts then the
     drawn token), p_at / q_at (p_i(x_i), q_i(x_i) for every i < gamma), status
     bits, flag_accept (positions whose test fell inside the band), edge (the
-    relative edge distance of the draw) and draw ("residual" or "bonus").
+    relative edge distance of the draw), draw ("residual", "residual_zero" or
+    "bonus") and weights (the unnormalised weights the draw used).
     """
     target = np.asarray(target, dtype=np.float64)
     draft = np.asarray(draft, dtype=np.float64)
@@ -199,7 +200,7 @@ def verify_chain_seq(target, draft, draft_tokens, uniforms, temperature, force=N
     tokens = [int(t) for t in toks[:k]] + [y]
     return {
         "k": k, "tokens": tokens, "p_at": p_at, "q_at": q_at, "status": status,
-        "flag_accept": flag_accept, "edge": edge, "draw": draw,
+        "flag_accept": flag_accept, "edge": edge, "draw": draw, "weights": w,
     }
 
 

@@ -1,0 +1,134 @@
+// C ABI of libspecverify: argument validation and dispatch to the kernel launchers.
+//
+// Nothing here allocates, synchronises or reads device memory: every check uses the
+// arguments alone, and all work is enqueued on the caller's stream.
+
+#include <stdint.h>
+
+#include "sv_internal.h"
+#include "specverify.h"
+
+#define SV_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int vec_width(sv_dtype dtype) { return dtype == SV_F32 ? 4 : 8; }
+
+bool valid_dtype(sv_dtype dtype) { return dtype == SV_F32 || dtype == SV_BF16; }
+
+// Grid sizes are 32-bit: one wave per (row, chunk), four waves per workgroup.
+bool grid_fits(int64_t rows, int64_t V) {
+  const int64_t waves = rows * sv::n_chunks(V);
+  return waves / 4 + 1 < int64_t(INT32_MAX);
+}
+
+bool chain_shape_ok(int32_t B, int32_t gamma, int64_t V) {
+  if (B < 1 || B > sv::kMaxBatch || gamma < 1 || gamma > sv::kMaxGamma) return false;
+  if (V < 1 || V > int64_t(INT32_MAX)) return false;
+  return grid_fits(int64_t(B) * (2 * gamma + 1), V);
+}
+
+bool tree_shape_ok(int32_t n_trees, int32_t n_nodes, int64_t V) {
+  if (n_trees < 1 || n_trees > sv::kMaxBatch || n_nodes < 1 || n_nodes > sv::kMaxTreeNodes)
+    return false;
+  if (V < 1 || V > int64_t(INT32_MAX)) return false;
+  return grid_fits(int64_t(n_trees) * n_nodes, V);
+}
+
+}  // namespace
+
+SV_EXPORT const char* sv_version(void) { return "specverify 0.1.0 gfx950"; }
+
+SV_EXPORT const char* sv_status_string(sv_status status) {
+  switch (status) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_NULL: return "SV_ERR_NULL: a required pointer is NULL";
+    case SV_ERR_SHAPE: return "SV_ERR_SHAPE: a size is out of range";
+    case SV_ERR_DTYPE: return "SV_ERR_DTYPE: unknown logit dtype";
+    case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case SV_ERR_LAUNCH: return "SV_ERR_LAUNCH: kernel launch failed";
+  }
+  return "unknown sv_status";
+}
+
+SV_EXPORT size_t sv_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
+                                                 sv_dtype dtype) {
+  if (!valid_dtype(dtype) || !chain_shape_ok(B, gamma, V)) return 0;
+  return sv::chain_layout(B, gamma, V).total;
+}
+
+SV_EXPORT sv_status sv_verify_chain(const void* target_logits, const void* draft_logits,
+                                    sv_dtype dtype, const int32_t* draft_tokens,
+                                    const float* uniforms, const float* temperature, int32_t B,
+                                    int32_t gamma, int64_t V, int32_t* out_tokens,
+                                    int32_t* out_num_accepted, float* out_p, float* out_q,
+                                    int32_t* out_status, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !temperature ||
+      !out_tokens || !out_num_accepted)
+    return SV_ERR_NULL;
+  if (!valid_dtype(dtype)) return SV_ERR_DTYPE;
+  if (!chain_shape_ok(B, gamma, V)) return SV_ERR_SHAPE;
+  const size_t need = sv::chain_layout(B, gamma, V).total;
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SV_ERR_WORKSPACE;
+
+  sv::ChainArgs a;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.dtype = dtype;
+  a.draft_tokens = draft_tokens;
+  a.uniforms = uniforms;
+  a.temperature = temperature;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.out_tokens = out_tokens;
+  a.out_num_accepted = out_num_accepted;
+  a.out_p = out_p;
+  a.out_q = out_q;
+  a.out_status = out_status;
+  a.ws = static_cast<char*>(workspace);
+  a.vec = aligned16(target_logits) && aligned16(draft_logits) && V % vec_width(dtype) == 0;
+  return sv::launch_chain(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+SV_EXPORT size_t sv_verify_tree_workspace_bytes(int32_t n_trees, int32_t n_nodes, int64_t V,
+                                                sv_dtype dtype) {
+  if (!valid_dtype(dtype) || !tree_shape_ok(n_trees, n_nodes, V)) return 0;
+  return sv::tree_layout(n_trees, n_nodes, V).total;
+}
+
+SV_EXPORT sv_status sv_verify_tree(const void* logits, sv_dtype dtype, const int32_t* parents,
+                                   const int32_t* node_tokens, int32_t n_trees, int32_t n_nodes,
+                                   int64_t V, int32_t* out_path, int32_t* out_tokens,
+                                   int32_t* out_num_accepted, int32_t* out_node_argmax,
+                                   int32_t* out_status, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  if (!logits || !parents || !node_tokens || !out_path || !out_tokens || !out_num_accepted)
+    return SV_ERR_NULL;
+  if (!valid_dtype(dtype)) return SV_ERR_DTYPE;
+  if (!tree_shape_ok(n_trees, n_nodes, V)) return SV_ERR_SHAPE;
+  const size_t need = sv::tree_layout(n_trees, n_nodes, V).total;
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SV_ERR_WORKSPACE;
+
+  sv::TreeArgs a;
+  a.logits = logits;
+  a.dtype = dtype;
+  a.parents = parents;
+  a.node_tokens = node_tokens;
+  a.n_trees = n_trees;
+  a.n_nodes = n_nodes;
+  a.V = V;
+  a.out_path = out_path;
+  a.out_tokens = out_tokens;
+  a.out_num_accepted = out_num_accepted;
+  a.out_node_argmax = out_node_argmax;
+  a.out_status = out_status;
+  a.ws = static_cast<char*>(workspace);
+  a.vec = aligned16(logits) && V % vec_width(dtype) == 0;
+  return sv::launch_tree(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}

@@ -1,0 +1,160 @@
+// Device-side building blocks: exact logit widening, chunk loads, wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+// ---------------------------------------------------------------------------- widening
+
+// bf16 is the upper half of an fp32 word: widening is a 16-bit shift, exact.
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// ---------------------------------------------------------------------------- chunk loads
+//
+// A chunk is kChunk consecutive elements of one logit row.  Lane `lane` of the
+// wave that owns chunk c issues kElemsPerLane / VW loads of VW elements each;
+// load j covers the VW elements starting at chunk offset (j * 64 + lane) * VW,
+// so every load instruction reads 64 * VW consecutive elements (1 KiB for the
+// 16-byte vector forms).  Element (j, t) of a lane lands in z[j * VW + t]; the
+// chunk's element order is (j, lane, t) lexicographic.  Elements at or beyond V
+// are not read and are set to -inf.
+//
+// VW = 4 (fp32) and VW = 8 (bf16) are 16-byte loads and require a 16-byte
+// aligned row start and V % VW == 0 (checked on the host); VW = 1 reads one
+// element per load and has no alignment requirement.
+
+template <typename T, int VW>
+struct Vec;
+template <>
+struct Vec<float, 4> {
+  using type = float4;
+};
+template <>
+struct Vec<uint16_t, 8> {
+  using type = uint4;
+};
+
+template <typename T, int VW>
+__device__ __forceinline__ void unpack(const typename Vec<T, VW>::type& v, float* out);
+
+template <>
+__device__ __forceinline__ void unpack<float, 4>(const float4& v, float* out) {
+  out[0] = v.x;
+  out[1] = v.y;
+  out[2] = v.z;
+  out[3] = v.w;
+}
+
+template <>
+__device__ __forceinline__ void unpack<uint16_t, 8>(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Chunk offset (in elements) of element (j, t) of `lane`.
+template <int VW>
+__device__ __forceinline__ int chunk_offset(int j, int lane, int t) {
+  return (j * kWave + lane) * VW + t;
+}
+
+template <typename T, int VW>
+__device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t V, int64_t c, int lane,
+                                           float (&z)[kElemsPerLane]) {
+  constexpr int NLD = kElemsPerLane / VW;
+  const int64_t c0 = c * kChunk;
+  if constexpr (VW == 1) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int64_t e = c0 + j * kWave + lane;
+      z[j] = e < V ? widen(row[e]) : -INFINITY;
+    }
+  } else {
+    using VT = typename Vec<T, VW>::type;
+    const VT* vrow = reinterpret_cast<const VT*>(row);
+    const int64_t nvec = V / VW;
+    const int64_t v0 = c0 / VW;
+    VT buf[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int64_t vi = v0 + j * kWave + lane;
+      if (vi < nvec) buf[j] = vrow[vi];
+    }
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int64_t vi = v0 + j * kWave + lane;
+      if (vi < nvec) {
+        unpack<T, VW>(buf[j], &z[j * VW]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < VW; ++t) z[j * VW + t] = -INFINITY;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- wave collectives
+// Butterfly (xor) reductions: every lane ends with the same, bitwise identical value.
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Inclusive prefix sum over the lanes of a wave (Hillis-Steele).
+__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_broadcast(double v, int src) { return __shfl(v, src, kWave); }
+
+// 2^x on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The temperature used for arithmetic: T itself when finite and positive, else 1.  A sequence
+// with an invalid T is reported and takes the fallback result; substituting 1 keeps its row
+// statistics meaningful, so the logit checks (NaN, +inf, all -inf) do not depend on T.
+__device__ __forceinline__ float effective_temperature(float T) {
+  return (T > 0.0f && T < INFINITY) ? T : 1.0f;
+}
+
+// log2(e) / T in fp32, correctly rounded; every kernel forms it the same way so that
+// per-element terms recomputed in a later kernel are bitwise identical.  Clamped to the
+// largest finite float so that a tiny T gives (z - m) * k = 0 (not NaN) at the maximum.
+__device__ __forceinline__ float log2e_over_t(float T) {
+  return fminf(1.4426950408889634f / T, 3.40282347e38f);
+}
+
+}  // namespace sv

@@ -1,0 +1,131 @@
+// Internal declarations shared by the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+// One wavefront (64 lanes) sweeps one "chunk" of a logit row: every lane holds
+// kElemsPerLane consecutive-in-vector elements spread over kElemsPerLane/VEC
+// coalesced 16-byte loads.  Chunks are the unit of the per-row partial
+// statistics kept in the workspace.
+constexpr int kWave = 64;
+constexpr int kElemsPerLane = 32;
+constexpr int kChunk = kWave * kElemsPerLane;  // elements per chunk (2048)
+constexpr int kMaxGamma = 64;
+constexpr int kMaxTreeNodes = 4096;
+constexpr int kMaxBatch = 1 << 24;
+
+inline int64_t n_chunks(int64_t V) { return (V + kChunk - 1) / kChunk; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Per (row, chunk) softmax partial: chunk max m and sum_x exp((z(x) - m) / T) in fp64.
+struct __attribute__((aligned(16))) RowPart {
+  float m;
+  int32_t pad;
+  double s;
+};
+
+// Per row merged statistics: row max and sum_x exp((z(x) - max) / T).
+struct __attribute__((aligned(16))) RowStat {
+  float m;
+  int32_t valid;
+  double s;
+};
+
+// Per sequence decision written by the decide kernel.
+enum DrawMode : int32_t { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2 };
+struct __attribute__((aligned(16))) SeqDecision {
+  int32_t k;       // drafts accepted
+  int32_t mode;    // DrawMode
+  int32_t status;  // SV_ROW_* bits so far
+  int32_t pad;
+};
+
+// Per (row, chunk) argmax partial for the tree path.
+struct __attribute__((aligned(16))) ArgPart {
+  float v;       // chunk maximum over non-NaN entries (-inf if none)
+  int32_t idx;   // lowest index attaining it (INT32_MAX if none)
+  int32_t nan;   // chunk holds a NaN
+  int32_t pad;
+};
+
+struct ChainLayout {
+  int64_t nchunk;
+  size_t off_part, off_rowstat, off_seq, off_wres, total;
+};
+
+inline ChainLayout chain_layout(int64_t B, int64_t gamma, int64_t V) {
+  ChainLayout L;
+  L.nchunk = n_chunks(V);
+  const int64_t rows = B * (2 * gamma + 1);
+  size_t off = 0;
+  L.off_part = off;
+  off += align256(sizeof(RowPart) * size_t(rows) * size_t(L.nchunk));
+  L.off_rowstat = off;
+  off += align256(sizeof(RowStat) * size_t(rows));
+  L.off_seq = off;
+  off += align256(sizeof(SeqDecision) * size_t(B));
+  L.off_wres = off;
+  off += align256(sizeof(double) * size_t(B) * size_t(L.nchunk));
+  L.total = off;
+  return L;
+}
+
+struct TreeLayout {
+  int64_t nchunk;
+  size_t off_part, total;
+};
+
+inline TreeLayout tree_layout(int64_t n_trees, int64_t n_nodes, int64_t V) {
+  TreeLayout L;
+  L.nchunk = n_chunks(V);
+  L.off_part = 0;
+  L.total = align256(sizeof(ArgPart) * size_t(n_trees) * size_t(n_nodes) * size_t(L.nchunk));
+  return L;
+}
+
+struct ChainArgs {
+  const void* target;
+  const void* draft;
+  sv_dtype dtype;
+  const int32_t* draft_tokens;
+  const float* uniforms;
+  const float* temperature;
+  int32_t B, gamma;
+  int64_t V;
+  int32_t* out_tokens;
+  int32_t* out_num_accepted;
+  float* out_p;
+  float* out_q;
+  int32_t* out_status;
+  char* ws;
+  bool vec;  // 16-byte vector-load path is legal
+};
+
+struct TreeArgs {
+  const void* logits;
+  sv_dtype dtype;
+  const int32_t* parents;
+  const int32_t* node_tokens;
+  int32_t n_trees, n_nodes;
+  int64_t V;
+  int32_t* out_path;
+  int32_t* out_tokens;
+  int32_t* out_num_accepted;
+  int32_t* out_node_argmax;
+  int32_t* out_status;
+  char* ws;
+  bool vec;
+};
+
+// Launch the chain kernels on `stream`; returns hipSuccess or the launch error.
+hipError_t launch_chain(const ChainArgs& a, hipStream_t stream);
+hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
+
+}  // namespace sv

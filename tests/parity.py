@@ -1,0 +1,124 @@
+"""GPU-versus-oracle comparison rules (shared by the parity tests, the smoke check and the bench).
+
+Integer outputs must be bit-exact, except where the oracle itself reports that fp32-level
+rounding may flip the decision:
+
+* an accept test with |u - min(1, p/q)| < 1e-6: the GPU result must equal the oracle
+  replayed with either decision at each such position;
+* a draw with u*W within 1e-6*W of a bucket edge: the GPU token must be the oracle's or the
+  nearest token with positive weight across that edge.
+
+Probabilities p_i(x_i), q_i(x_i) must satisfy |gpu - ref| <= 1e-5 * ref + 1e-30.
+"""
+
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+from oracle import chain as OC
+from oracle import tree as OT
+
+P_RTOL = 1e-5
+P_ATOL = 1e-30
+
+
+def _neighbours(res):
+    """Tokens the draw may legitimately return for an edge-flagged oracle result."""
+    y = res["tokens"][-1]
+    w = res["weights"]
+    out = {y}
+    pos = np.flatnonzero(w > 0)
+    lower = pos[pos < y]
+    upper = pos[pos > y]
+    if len(lower):
+        out.add(int(lower[-1]))
+    if len(upper):
+        out.add(int(upper[0]))
+    return out
+
+
+def allowed_outcomes(target, draft, toks, uni, temp, res):
+    """(k, tokens) pairs the GPU may return for this sequence, with a flag kind."""
+    kind = "exact"
+    cands = [res]
+    if res["flag_accept"]:
+        kind = "accept_band"
+        cands = []
+        flagged = res["flag_accept"]
+        for bits in itertools.product([False, True], repeat=len(flagged)):
+            force = dict(zip(flagged, bits))
+            cands.append(OC.verify_chain_seq(target, draft, toks, uni, temp, force=force))
+    allowed = set()
+    for r in cands:
+        if r["edge"] < OC.BAND:
+            if kind == "exact":
+                kind = "edge_band"
+            for y in _neighbours(r):
+                allowed.add((r["k"], tuple(r["tokens"][:-1]) + (y,)))
+        else:
+            allowed.add((r["k"], tuple(r["tokens"])))
+    return allowed, kind
+
+
+def check_chain(batch, out, seqs=None):
+    """Compare GPU chain outputs (numpy arrays) with the oracle on the listed sequences.
+
+    out: dict with tokens [B, gamma+1], num_accepted [B], p, q [B, gamma], status [B].
+    Returns counts {"exact": n, "accept_band": n, "edge_band": n, "fallback": n}.
+    Raises AssertionError with a description on the first mismatch.
+    """
+    B, gamma = batch.B, batch.gamma
+    seqs = range(B) if seqs is None else seqs
+    counts = {"exact": 0, "accept_band": 0, "edge_band": 0, "fallback": 0}
+    for b in seqs:
+        zt = OC.widen(batch.target[b], batch.dtype)
+        zd = OC.widen(batch.draft[b], batch.dtype)
+        toks, uni, temp = batch.draft_tokens[b], batch.uniforms[b], batch.temperature[b]
+        res = OC.verify_chain_seq(zt, zd, toks, uni, temp)
+        st = int(out["status"][b])
+        assert st == res["status"], f"seq {b}: status {st} != oracle {res['status']}"
+        k = int(out["num_accepted"][b])
+        row = [int(x) for x in out["tokens"][b]]
+        assert all(x == -1 for x in row[k + 1:]), f"seq {b}: padding {row}"
+        if res["status"] & OC.FALLBACK_BITS:
+            assert k == 0 and row[0] == 0, f"seq {b}: fallback expected, got k={k} {row}"
+            counts["fallback"] += 1
+            continue
+        # probabilities
+        for name, ref in (("p", res["p_at"]), ("q", res["q_at"])):
+            got = np.asarray(out[name][b], dtype=np.float64)
+            err = np.abs(got - ref)
+            lim = P_RTOL * np.abs(ref) + P_ATOL
+            bad = np.flatnonzero(~(err <= lim))
+            assert len(bad) == 0, (f"seq {b}: {name}[{bad[0]}] gpu {got[bad[0]]!r} "
+                                   f"oracle {ref[bad[0]]!r}")
+        allowed, kind = allowed_outcomes(zt, zd, toks, uni, temp, res)
+        got = (k, tuple(row[:k + 1]))
+        assert got in allowed, (f"seq {b} ({kind}): gpu k={k} tokens={row[:k + 1]} "
+                                f"oracle k={res['k']} tokens={res['tokens']} "
+                                f"edge={res['edge']:.3g} flags={res['flag_accept']}")
+        counts[kind] += 1
+    return counts
+
+
+def check_tree(batch, out, trees=None):
+    """Compare GPU tree outputs with the oracle: bit-exact path, tokens, k, argmax, status."""
+    n = batch.n_nodes
+    trees = range(batch.n_trees) if trees is None else trees
+    accepted = []
+    for t in trees:
+        res = OT.verify_tree_one(OC.widen(batch.logits[t], batch.dtype), batch.parents[t],
+                                 batch.node_tokens[t])
+        k = res["k"]
+        assert int(out["status"][t]) == res["status"], f"tree {t}: status"
+        assert int(out["num_accepted"][t]) == k, f"tree {t}: k {out['num_accepted'][t]} != {k}"
+        path = list(res["path"]) + [-1] * (n - len(res["path"]))
+        toks = list(res["tokens"]) + [-1] * (n - len(res["tokens"]))
+        assert [int(x) for x in out["path"][t]] == path, f"tree {t}: path"
+        assert [int(x) for x in out["tokens"][t]] == toks, f"tree {t}: tokens"
+        if out.get("node_argmax") is not None:
+            assert [int(x) for x in out["node_argmax"][t]] == res["g"], f"tree {t}: argmax"
+        accepted.append(k)
+    return accepted

@@ -1,0 +1,104 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and its host-side
+validation rejects bad arguments before anything is launched (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from rejection_sampling_verify_chain_amd import binding as BD
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(BD.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = BD.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert BD.version().startswith("specverify") and "gfx950" in BD.version()
+    for st in (BD.SV_OK, BD.SV_ERR_NULL, BD.SV_ERR_SHAPE, BD.SV_ERR_DTYPE, BD.SV_ERR_WORKSPACE,
+               BD.SV_ERR_LAUNCH):
+        assert BD.status_string(st).startswith("SV_")
+    assert BD.status_string(99) == "unknown sv_status"
+
+
+def test_workspace_sizes():
+    lib = BD.load()
+    f = lib.sv_verify_chain_workspace_bytes
+    n = f(256, 7, 152064, BD.SV_F32)
+    # per-chunk partials dominate: 3840 rows x 75 chunks x 16 bytes
+    assert n >= 3840 * 75 * 16 and n % 256 == 0
+    assert f(0, 4, 1000, BD.SV_F32) == 0 and f(1, 0, 1000, BD.SV_F32) == 0
+    assert f(1, 65, 1000, BD.SV_F32) == 0 and f(1, 4, 0, BD.SV_F32) == 0
+    assert f(1, 4, 1000, 7) == 0
+    g = lib.sv_verify_tree_workspace_bytes
+    assert g(16, 64, 32000, BD.SV_BF16) >= 16 * 64 * 16 * 16
+    assert g(16, 4097, 32000, BD.SV_BF16) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def chain_call(**kw):
+    a = dict(target=FAKE, draft=FAKE, dtype=BD.SV_F32, toks=FAKE, uni=FAKE, temp=FAKE, B=1,
+             gamma=4, V=1000, out_tokens=FAKE, out_nacc=FAKE, out_p=None, out_q=None,
+             out_status=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return BD.load().sv_verify_chain(*a.values())
+
+
+def tree_call(**kw):
+    a = dict(logits=FAKE, dtype=BD.SV_BF16, parents=FAKE, tokens=FAKE, n_trees=1, n_nodes=8,
+             V=100, out_path=FAKE, out_tokens=FAKE, out_nacc=FAKE, out_g=None, out_status=None,
+             ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return BD.load().sv_verify_tree(*a.values())
+
+
+@pytest.mark.parametrize("field", ["target", "draft", "toks", "uni", "temp", "out_tokens",
+                                   "out_nacc"])
+def test_chain_null_pointers(field):
+    assert chain_call(**{field: None}) == BD.SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), BD.SV_ERR_DTYPE),
+    (dict(B=0), BD.SV_ERR_SHAPE), (dict(B=1 << 25), BD.SV_ERR_SHAPE),
+    (dict(gamma=0), BD.SV_ERR_SHAPE), (dict(gamma=65), BD.SV_ERR_SHAPE),
+    (dict(V=0), BD.SV_ERR_SHAPE), (dict(V=1 << 31), BD.SV_ERR_SHAPE),
+    (dict(ws=None), BD.SV_ERR_WORKSPACE), (dict(ws_bytes=16), BD.SV_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x1010)), BD.SV_ERR_WORKSPACE),
+])
+def test_chain_validation(kw, status):
+    assert chain_call(**kw) == status
+
+
+@pytest.mark.parametrize("field", ["logits", "parents", "tokens", "out_path", "out_tokens",
+                                   "out_nacc"])
+def test_tree_null_pointers(field):
+    assert tree_call(**{field: None}) == BD.SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=-1), BD.SV_ERR_DTYPE),
+    (dict(n_trees=0), BD.SV_ERR_SHAPE), (dict(n_nodes=0), BD.SV_ERR_SHAPE),
+    (dict(n_nodes=4097), BD.SV_ERR_SHAPE), (dict(V=0), BD.SV_ERR_SHAPE),
+    (dict(ws=None), BD.SV_ERR_WORKSPACE), (dict(ws_bytes=0), BD.SV_ERR_WORKSPACE),
+])
+def test_tree_validation(kw, status):
+    assert tree_call(**kw) == status

@@ -1,0 +1,191 @@
+"""GPU parity of sv_verify_chain against the oracle (through the C ABI)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+from scipy.special import softmax as sp_softmax
+
+from parity import check_chain
+from rejection_sampling_verify_chain_amd import binding as BD
+from rejection_sampling_verify_chain_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_chain(batch, offset=0):
+    """Run the library on a ChainBatch; offset > 0 shifts the logit base pointers by that many
+    elements (an unaligned view of a larger buffer)."""
+    d = BD.chain_to_device(batch)
+    tgt, drf = d["target"], d["draft"]
+    if offset:
+        def shifted(t):
+            flat = torch.empty(t.numel() + offset, dtype=t.dtype, device=t.device)
+            v = flat[offset:].view(t.shape)
+            v.copy_(t)
+            return v
+        tgt, drf = shifted(tgt), shifted(drf)
+    out = BD.sv_verify_chain(tgt, drf, d["draft_tokens"], d["uniforms"], d["temperature"])
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def report(name, counts):
+    print(f"[parity] {name}: {counts}", flush=True)
+
+
+def test_c1():
+    b = I.chain_c1()
+    report("c1", check_chain(b, run_chain(b)))
+
+
+@pytest.mark.parametrize("gamma", [4, 5, 6, 7])
+def test_c2(gamma):
+    b = I.chain_c2(gamma=gamma)
+    report(f"c2 gamma={gamma}", check_chain(b, run_chain(b)))
+
+
+def test_c3_full():
+    b = I.chain_c3()
+    counts = check_chain(b, run_chain(b))
+    report("c3", counts)
+    assert counts["exact"] >= 48  # bands are rare; the bulk must match exactly
+
+
+def test_c4_full_size_sampled():
+    # Full workload, launched exactly as the benchmark launches it; the oracle checks a sample
+    # of sequences covering both temperatures.
+    b = I.chain_c4()
+    out = run_chain(b)
+    seqs = list(range(0, 256, 8)) + [1, 2, 3, 255]
+    counts = check_chain(b, out, seqs)
+    report("c4 sampled", counts)
+    k = out["num_accepted"]
+    assert np.all((k >= 0) & (k <= 7))
+    assert np.all((out["tokens"][np.arange(256), k] >= 0) & (out["tokens"][np.arange(256), k] < 152064))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 7, 63, 64, 65, 1000, 2047, 2048, 2049, 4100, 5003, 8191])
+def test_edge_shapes(dtype, V):
+    for B, gamma, T in ((1, 1, 1.0), (3, 2, 0.5), (17, 7, 2.0)):
+        b = I.chain_gaussian(V * 31 + B, B, gamma, V, dtype, 2.0, 1.0, T)
+        report(f"gauss {dtype} V={V} B={B} g={gamma}", check_chain(b, run_chain(b)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unaligned_base_pointer(dtype):
+    b = I.chain_gaussian(5, 4, 3, 4096, dtype, 2.0, 1.0, 1.0)
+    report(f"unaligned {dtype}", check_chain(b, run_chain(b, offset=1)))
+
+
+def test_gamma_max_and_all_accept():
+    # draft == target: every token is accepted; gamma = 64 exercises the full-wave mask.
+    rng = np.random.default_rng(0)
+    t = rng.normal(scale=2.0, size=(2, 65, 300)).astype(np.float32)
+    b = I.chain_from_logits(6, t, t[:, :64], 0.9)
+    out = run_chain(b)
+    assert np.all(out["num_accepted"] == 64)
+    report("gamma=64 p==q", check_chain(b, out))
+
+
+def test_masked_logits_and_disjoint_support():
+    rng = np.random.default_rng(1)
+    B, g, V = 6, 3, 3000
+    t = rng.normal(scale=2.0, size=(B, g + 1, V)).astype(np.float32)
+    d = (t[:, :g] + rng.normal(size=(B, g, V))).astype(np.float32)
+    t[rng.random(t.shape) < 0.3] = -np.inf
+    d[rng.random(d.shape) < 0.3] = -np.inf
+    d[0, 0, :1500] = -np.inf  # disjoint supports at sequence 0, position 0
+    t[0, 0, 1500:] = -np.inf
+    b = I.chain_from_logits(7, t, d, 1.0)
+    out = run_chain(b)
+    assert out["num_accepted"][0] == 0 and out["tokens"][0, 0] < 1500
+    report("masked", check_chain(b, out))
+
+
+def test_data_errors_set_flags():
+    b = I.chain_gaussian(8, 6, 3, 500, "f32", 2.0, 1.0, 1.0)
+    b.draft_tokens[0, 1] = 500
+    b.target[1, 2, 17] = np.nan
+    b.draft[2, 0, :] = -np.inf
+    b.temperature[3] = 0.0
+    b.uniforms[4, 3] = 1.0
+    b.target[5, 0, 3] = np.inf
+    out = run_chain(b)
+    want = [BD.ROW_TOKEN_RANGE, BD.ROW_NONFINITE, BD.ROW_NONFINITE, BD.ROW_BAD_TEMPERATURE,
+            BD.ROW_BAD_UNIFORM, BD.ROW_NONFINITE]
+    assert list(out["status"]) == want
+    assert np.all(out["num_accepted"] == 0) and np.all(out["tokens"][:, 0] == 0)
+    report("data errors", check_chain(b, out))
+
+
+def test_golden_sequence_diagram():
+    g = json.load(open(os.path.join(GOLDEN, "p1_sequence_diagram.json")))
+    s = g["scripted"]
+    t = np.log(np.array(s["target_probs"], dtype=np.float32))[None]
+    d = np.log(np.array(s["draft_probs"], dtype=np.float32))[None]
+    b = I.chain_from_logits(0, t, d, s["temperature"])
+    b.draft_tokens[0] = s["draft_tokens"]
+    b.uniforms[0] = s["uniforms"]
+    out = run_chain(b)
+    assert int(out["num_accepted"][0]) == g["expected"]["num_accepted"]
+    assert list(out["tokens"][0, :3]) == g["expected"]["tokens"]
+
+
+def test_deterministic():
+    b = I.chain_c2(gamma=7)
+    o1, o2 = run_chain(b), run_chain(b)
+    for k in o1:
+        assert np.array_equal(o1[k], o2[k]), k
+
+
+def _many(zt, zd, T, N, seed):
+    """N sequences sharing the logits, with draft tokens drawn from q and fresh uniforms."""
+    rng = np.random.default_rng(seed)
+    g, V = zd.shape
+    t = np.broadcast_to(zt.astype(np.float32), (N, g + 1, V)).copy()
+    d = np.broadcast_to(zd.astype(np.float32), (N, g, V)).copy()
+    b = I.chain_from_logits(seed, t, d, T)
+    return b
+
+
+def test_theorem1_on_gpu_outputs():
+    rng = np.random.default_rng(2)
+    V, g, T = 6, 3, 0.8
+    zt = rng.normal(size=(g + 1, V))
+    zd = zt[:g] + rng.normal(size=(g, V))
+    b = _many(zt, zd, T, 200000, 3)
+    out = run_chain(b)
+    ks, toks = out["num_accepted"], out["tokens"]
+    zt32 = zt.astype(np.float32).astype(np.float64)
+    for j in range(g + 1):
+        sel = ks >= j
+        obs = np.bincount(toks[sel, j], minlength=V)
+        pv = stats.chisquare(obs, sp_softmax(zt32[j] / T) * sel.sum()).pvalue
+        assert pv > 1e-3, (j, pv)
+
+
+def test_closed_form_on_gpu_outputs():
+    g, a, bq = 5, 0.6, 0.3
+    alpha = 1 - abs(a - bq)
+    zt = np.log(np.array([[a, 1 - a]] * (g + 1)))
+    zd = np.log(np.array([[bq, 1 - bq]] * g))
+    b = _many(zt, zd, 1.0, 200000, 4)
+    ks = run_chain(b)["num_accepted"].astype(np.int64)
+    emitted = ks + 1
+    expect = (1 - alpha ** (g + 1)) / (1 - alpha)
+    se = emitted.std(ddof=1) / np.sqrt(len(emitted))
+    assert abs(emitted.mean() - expect) < 4 * se
+    probs = np.array([alpha ** k * (1 - alpha) for k in range(g)] + [alpha ** g])
+    assert stats.chisquare(np.bincount(ks, minlength=g + 1), probs * len(ks)).pvalue > 1e-3
+
+
+@pytest.mark.parametrize("T", [1e-30, 1.4e-45, 1e-3, 50.0, 1e30])
+def test_extreme_temperatures(T):
+    b = I.chain_gaussian(9, 5, 4, 777, "f32", 2.0, 1.0, T)
+    report(f"T={T}", check_chain(b, run_chain(b)))

@@ -1,0 +1,108 @@
+"""GPU parity of sv_verify_tree against the oracle (through the C ABI)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from parity import check_tree
+from rejection_sampling_verify_chain_amd import binding as BD
+from rejection_sampling_verify_chain_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_tree(batch, offset=0):
+    d = BD.tree_to_device(batch)
+    logits = d["logits"]
+    if offset:
+        flat = torch.empty(logits.numel() + offset, dtype=logits.dtype, device=logits.device)
+        v = flat[offset:].view(logits.shape)
+        v.copy_(logits)
+        logits = v
+    out = BD.sv_verify_tree(logits, d["parents"], d["node_tokens"])
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def test_c5():
+    b = I.tree_c5()
+    ks = check_tree(b, run_tree(b))
+    print(f"[parity] c5 accepted per tree: {ks}", flush=True)
+
+
+def test_c5_shape_deep_acceptance():
+    # Same shape as c5 with a boost large enough that most walks go deep.
+    b = I.tree_random(15, 16, 64, 32000, "bf16", boost=20.0, boost_prob=1.0)
+    ks = check_tree(b, run_tree(b))
+    print(f"[parity] deep accepted per tree: {ks}", flush=True)
+    assert max(ks) >= 4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,n_nodes", [(1, 1), (5, 3), (8, 64), (8, 65), (300, 130),
+                                       (2049, 17), (5003, 40)])
+def test_random_trees_with_ties(dtype, V, n_nodes):
+    rng = np.random.default_rng(V * 7 + n_nodes)
+    n_trees = 9
+    b = I.tree_random(V + n_nodes, n_trees, n_nodes, V, dtype, boost=0.0, boost_prob=0.0,
+                      max_branch=min(4, V), max_depth=n_nodes)
+    # integer logits make ties frequent; boosts make matches frequent
+    z = rng.integers(-3, 3, size=b.logits.shape).astype(np.float32)
+    for t in range(n_trees):
+        for u in range(n_nodes):
+            kids = np.flatnonzero(b.parents[t] == u)
+            if len(kids) and rng.random() < 0.8:
+                z[t, u, b.node_tokens[t, kids[0]]] = 5.0
+    b.logits = I.bf16_bits(z) if dtype == "bf16" else z
+    check_tree(b, run_tree(b))
+
+
+def test_unaligned_and_signed_zero():
+    b = I.tree_random(21, 4, 16, 4096, "bf16")
+    z = I.bf16_value(b.logits).copy()
+    z[:, :, :] = -1.0
+    z[0, 0, 10] = -0.0
+    z[0, 0, 5] = 0.0  # +0 at a lower index than -0: both are the maximum, lowest index wins
+    b.logits = I.bf16_bits(z)
+    out = run_tree(b, offset=3)
+    assert out["node_argmax"][0, 0] == 5
+    check_tree(b, out)
+
+
+def test_golden_greedy_example():
+    g = json.load(open(os.path.join(GOLDEN, "p2_greedy_example.json")))
+    t = g["tree"]
+    V = len(g["vocab"])
+    n = len(t["parents"])
+    z = np.zeros((1, n, V), dtype=np.float32)
+    for u, c in enumerate(t["target_choice_per_node"]):
+        z[0, u, c] = 5.0
+    b = I.TreeBatch("p2", "f32", z, np.array([t["parents"]], dtype=np.int32),
+                    np.array([t["node_tokens"]], dtype=np.int32))
+    out = run_tree(b)
+    assert list(out["path"][0, :3]) == g["expected"]["path"]
+    assert list(out["tokens"][0, :3]) == g["expected"]["tokens"]
+    assert int(out["num_accepted"][0]) == g["expected"]["num_accepted"]
+
+
+def test_bad_trees_and_nan():
+    b = I.tree_random(22, 4, 10, 100, "f32")
+    b.parents[0, 5] = 7          # parent after child
+    b.parents[1, 0] = 0          # root must have parent -1
+    b.node_tokens[2, 3] = 100    # token out of range
+    b.logits[3, 2, 9] = np.nan   # NaN: flagged, walk proceeds
+    out = run_tree(b)
+    assert list(out["status"]) == [BD.ROW_BAD_TREE, BD.ROW_BAD_TREE, BD.ROW_TOKEN_RANGE,
+                                   BD.ROW_NONFINITE]
+    check_tree(b, out)
+
+
+def test_deterministic():
+    b = I.tree_c5()
+    o1, o2 = run_tree(b), run_tree(b)
+    for k in o1:
+        assert np.array_equal(o1[k], o2[k]), k
