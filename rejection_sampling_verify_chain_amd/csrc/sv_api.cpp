@@ -18,23 +18,23 @@ int vec_width(sv_dtype dtype) { return dtype == SV_F32 ? 4 : 8; }
 
 bool valid_dtype(sv_dtype dtype) { return dtype == SV_F32 || dtype == SV_BF16; }
 
-// Grid sizes are 32-bit: one wave per (row, chunk), four waves per workgroup.
-bool grid_fits(int64_t rows, int64_t V) {
-  const int64_t waves = rows * sv::n_chunks(V);
-  return waves / 4 + 1 < int64_t(INT32_MAX);
+// Grid sizes are 32-bit: `units` sequences (or trees) of `rows` logit rows each, one
+// workgroup per four (row, chunk) pairs of a unit.
+bool grid_fits(int64_t units, int64_t rows, int64_t V) {
+  return units * sv::groups_per_unit(rows, V) < int64_t(INT32_MAX);
 }
 
 bool chain_shape_ok(int32_t B, int32_t gamma, int64_t V) {
   if (B < 1 || B > sv::kMaxBatch || gamma < 1 || gamma > sv::kMaxGamma) return false;
   if (V < 1 || V > int64_t(INT32_MAX)) return false;
-  return grid_fits(int64_t(B) * (2 * gamma + 1), V);
+  return grid_fits(B, 2 * gamma + 1, V);  // the draw grid (one row per sequence) is smaller
 }
 
 bool tree_shape_ok(int32_t n_trees, int32_t n_nodes, int64_t V) {
   if (n_trees < 1 || n_trees > sv::kMaxBatch || n_nodes < 1 || n_nodes > sv::kMaxTreeNodes)
     return false;
   if (V < 1 || V > int64_t(INT32_MAX)) return false;
-  return grid_fits(int64_t(n_trees) * n_nodes, V);
+  return grid_fits(n_trees, n_nodes, V);
 }
 
 }  // namespace

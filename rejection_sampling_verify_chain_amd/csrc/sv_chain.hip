@@ -8,19 +8,19 @@
 // norm(max(0, p - q)), and the expected-speedup section the (gamma+1)-th token
 // of a fully accepted round.
 //
-// Pipeline (all on the caller's stream, no host synchronisation):
-//   1. rowstats  one wave per (row, chunk) of every logit row, target and draft:
-//                chunk max m_c and S_c = sum exp((z - m_c)/T) (fp32 terms, fp64 sum).
-//                This is the single HBM sweep over all B*(2*gamma+1)*V logits.
-//   2. decide    one workgroup per sequence: merges the chunk partials into the
-//                row max and normaliser, evaluates p_i(x_i), q_i(x_i) in fp64 (one
-//                lane per position), takes the accept bits with a ballot and the
-//                cut k = number of leading ones.
-//   3. residual  one wave per (sequence, chunk) of rejecting sequences: chunk mass
-//                W_c = sum max(0, p_k - q_k) over target and draft row k.
-//   4. draw      one wave per sequence: running sum over chunk masses (residual
-//                W_c, or the bonus row's p mass from step 1), locate the chunk
-//                holding u*W, re-scan that chunk in token order, write y.
+// Four launches per call, all on the caller's stream, no host synchronisation:
+//   sweep     the single HBM sweep over all B*(2*gamma+1)*V logits: each wave owns one chunk
+//             (2048 elements) of one logit row and writes its chunk max m_c and
+//             S_c = sum exp((z - m_c)/T) (fp32 terms, fp64 sum).
+//   decide    one workgroup per sequence merges the partials into each row's max and
+//             normaliser (fp64, one wave per row), evaluates p_i(x_i), q_i(x_i) in fp64 with
+//             one lane per position, and takes the cut k = number of leading accepts with one
+//             ballot.
+//   residual  one wave per chunk of a rejecting sequence sums the residual max(0, p_k - q_k)
+//             over that chunk of target row k and draft row k.
+//   draw      one wave per sequence draws y by inverse CDF: a running sum over the chunk
+//             masses (the residual masses, or the bonus row's p masses from the sweep) locates
+//             the chunk holding u*W, and that chunk is rescanned in token order.
 
 #include <math.h>
 
@@ -31,8 +31,30 @@
 namespace sv {
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = 1024;  // sweep and decide
 constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kResidualBlock = 256;
+static_assert(kWavesPerBlock == kChunksPerGroup, "one chunk per wave");
+
+struct ChainParams {
+  const void* tgt;
+  const void* drf;
+  const int32_t* toks;
+  const float* uni;
+  const float* temp;
+  int gamma;
+  int64_t V;
+  int64_t nchunk;
+  RowPart* part;
+  RowStat* rowstat;
+  SeqDecision* seq;
+  double* wres;
+  int32_t* out_tokens;
+  int32_t* out_nacc;
+  float* out_p;
+  float* out_q;
+  int32_t* out_status;
+};
 
 template <typename T>
 __device__ __forceinline__ const T* chain_row(const T* tgt, const T* drf, int64_t b, int gamma,
@@ -62,31 +84,18 @@ __device__ __forceinline__ double residual_term(float zt, float zd, float mt, fl
   return d > 0.0 ? d : 0.0;
 }
 
-// ------------------------------------------------------------------------------------ 1. rowstats
+// ------------------------------------------------------------------------------------ sweep
+
+// One wave: chunk c of logit row `row` -> (chunk max, fp64 sum of exp((z - max)/T)).
 template <typename T, int VW>
-__global__ __launch_bounds__(kBlock) void k_chain_rowstats(const T* __restrict__ tgt,
-                                                           const T* __restrict__ drf,
-                                                           const float* __restrict__ temp,
-                                                           int gamma, int64_t V, int64_t nchunk,
-                                                           int64_t total_chunks,
-                                                           RowPart* __restrict__ part) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x / kWave);
-  if (w >= total_chunks) return;  // wave-uniform
-  const int R = 2 * gamma + 1;
-  const int64_t row = w / nchunk;
-  const int64_t c = w - row * nchunk;
-  const int64_t b = row / R;
-  const int j = int(row - b * R);
-
+__device__ __forceinline__ RowPart sweep_chunk(const T* __restrict__ row, int64_t V, int64_t c,
+                                               int lane, float k) {
   float z[kElemsPerLane];
-  load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, j, V), V, c, lane, z);
-
+  load_chunk<T, VW>(row, V, c, lane, z);
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kElemsPerLane; ++i) m = fmaxf(m, z[i]);
   m = wave_max(m);
-
   double s;
   if (m == -INFINITY) {
     // Only -inf (or NaN) in this chunk: its mass is zero unless a NaN poisons the row.
@@ -95,207 +104,15 @@ __global__ __launch_bounds__(kBlock) void k_chain_rowstats(const T* __restrict__
     for (int i = 0; i < kElemsPerLane; ++i) nan |= (z[i] != z[i]);
     s = __any(nan) ? NAN : 0.0;
   } else {
-    const float k = log2e_over_t(effective_temperature(temp[b]));
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int i = 0; i < kElemsPerLane; ++i) acc[i & 3] += double(softmax_term(z[i], m, k));
     s = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
   }
-  if (lane == 0) part[w] = RowPart{m, 0, s};
+  return RowPart{m, 0, s};
 }
 
-// ------------------------------------------------------------------------------------ 2. decide
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_chain_decide(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ toks,
-    const float* __restrict__ uni, const float* __restrict__ temp, int gamma, int64_t V,
-    int64_t nchunk, const RowPart* __restrict__ part, RowStat* __restrict__ rowstat,
-    SeqDecision* __restrict__ seq, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ out_nacc, float* __restrict__ out_p, float* __restrict__ out_q,
-    int32_t* __restrict__ out_status) {
-  __shared__ RowStat st[2 * kMaxGamma + 1];
-  const int64_t b = blockIdx.x;
-  const int R = 2 * gamma + 1;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const float tb = temp[b];
-  const float te = effective_temperature(tb);
-  const double Td = te;
-
-  // Merge chunk partials: M = max_c m_c, S = sum_c S_c exp((m_c - M)/T).
-  for (int j = wave; j < R; j += kWavesPerBlock) {
-    const RowPart* pp = part + (b * R + j) * nchunk;
-    float m = -INFINITY;
-    for (int64_t c = lane; c < nchunk; c += kWave) m = fmaxf(m, pp[c].m);
-    m = wave_max(m);
-    double s = 0.0;
-    const bool finite_max = (m > -INFINITY) && (m < INFINITY);
-    if (finite_max) {
-      for (int64_t c = lane; c < nchunk; c += kWave) {
-        const RowPart q = pp[c];
-        const double f = q.m == -INFINITY ? 0.0 : exp((double(q.m) - double(m)) / Td);
-        s += q.s * f;  // a NaN partial survives the zero factor
-      }
-    }
-    s = wave_sum(s);
-    const int valid = finite_max && (s > 0.0) && (s < INFINITY);
-    if (lane == 0) {
-      st[j] = RowStat{m, valid, s};
-      rowstat[b * R + j] = st[j];
-    }
-  }
-  __syncthreads();
-  if (wave != 0) return;
-
-  int status = 0;
-  if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
-  bool bad = false;
-  for (int i = lane; i <= gamma; i += kWave) {
-    const float u = uni[b * (gamma + 1) + i];
-    bad |= !(u >= 0.0f && u < 1.0f);
-  }
-  if (__any(bad)) status |= SV_ROW_BAD_UNIFORM;
-  int x = 0;
-  bad = false;
-  if (lane < gamma) {
-    x = toks[b * gamma + lane];
-    bad = (x < 0) || (int64_t(x) >= V);
-  }
-  if (__any(bad)) status |= SV_ROW_TOKEN_RANGE;
-  bad = false;
-  for (int j = lane; j < R; j += kWave) bad |= !st[j].valid;
-  if (__any(bad)) status |= SV_ROW_NONFINITE;
-
-  const bool fallback = (status & (SV_ROW_TOKEN_RANGE | SV_ROW_NONFINITE |
-                                   SV_ROW_BAD_TEMPERATURE | SV_ROW_BAD_UNIFORM)) != 0;
-  int k = 0;
-  bool accept = false;
-  if (!fallback) {
-    double p = 0.0, q = 0.0;
-    if (lane < gamma) {
-      const RowStat a = st[lane];
-      const RowStat d = st[gamma + 1 + lane];
-      const double zt = widen(chain_row(tgt, drf, b, gamma, lane, V)[x]);
-      const double zd = widen(chain_row(tgt, drf, b, gamma, gamma + 1 + lane, V)[x]);
-      p = exp((zt - double(a.m)) / Td) / a.s;
-      q = exp((zd - double(d.m)) / Td) / d.s;
-      const double u = uni[b * (gamma + 1) + lane];
-      if (q > 0.0) {
-        accept = u < fmin(1.0, p / q);
-      } else {
-        accept = (p > 0.0) && (u < 1.0);  // ratio +inf; p = q = 0 rejects
-      }
-      if (out_p) out_p[b * gamma + lane] = float(p);
-      if (out_q) out_q[b * gamma + lane] = float(q);
-    }
-    // Cut at the first rejection: k = number of leading ones of the accept mask.
-    const uint64_t rej = ~uint64_t(__ballot(accept && lane < gamma));
-    const int lead = rej == 0 ? kWave : __builtin_ctzll(rej);
-    k = lead < gamma ? lead : gamma;
-  } else if (lane < gamma) {
-    if (out_p) out_p[b * gamma + lane] = NAN;
-    if (out_q) out_q[b * gamma + lane] = NAN;
-  }
-
-  // Accepted prefix now; the drawn token at position k is written by the draw kernel.
-  for (int i = lane; i <= gamma; i += kWave) {
-    int32_t v = -1;
-    if (i < k) v = x;  // i < k <= gamma <= 64 only on the first pass, where lane i holds x_i
-    if (fallback && i == 0) v = 0;
-    out_tokens[b * (gamma + 1) + i] = v;
-  }
-  if (lane == 0) {
-    seq[b] = SeqDecision{k, fallback ? kDrawNone : (k < gamma ? kDrawResidual : kDrawBonus),
-                         status, 0};
-    if (fallback) {
-      out_nacc[b] = 0;
-      if (out_status) out_status[b] = status;
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------ 3. residual
-template <typename T, int VW>
-__global__ __launch_bounds__(kBlock) void k_chain_residual(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
-    int gamma, int64_t V, int64_t nchunk, int64_t total, const RowPart* __restrict__ part,
-    const RowStat* __restrict__ rowstat, const SeqDecision* __restrict__ seq,
-    double* __restrict__ wres) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x / kWave);
-  if (w >= total) return;
-  const int64_t b = w / nchunk;
-  const int64_t c = w - b * nchunk;
-  const SeqDecision d = seq[b];
-  if (d.mode != kDrawResidual) return;
-  const int R = 2 * gamma + 1;
-  const int jt = d.k, jd = gamma + 1 + d.k;
-  const RowPart pt = part[(b * R + jt) * nchunk + c];
-  const RowPart pd = part[(b * R + jd) * nchunk + c];
-  const float tb = temp[b];
-  const float te = effective_temperature(tb);
-  const double Td = te;
-  const double A = chunk_scale(pt.m, rowstat[b * R + jt], Td);
-  const double Bq = chunk_scale(pd.m, rowstat[b * R + jd], Td);
-  const float k = log2e_over_t(te);
-
-  float zt[kElemsPerLane], zd[kElemsPerLane];
-  load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jt, V), V, c, lane, zt);
-  load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jd, V), V, c, lane, zd);
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int i = 0; i < kElemsPerLane; ++i)
-    acc[i & 3] += residual_term(zt[i], zd[i], pt.m, pd.m, k, A, Bq);
-  const double s = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
-  if (lane == 0) wres[w] = s;
-}
-
-// ------------------------------------------------------------------------------------ 4. draw
-
-// Running sum over the chunk masses of one sequence in chunk order.  Pass 1 returns the
-// total; pass 2 (same association, hence the same bits) finds the first chunk whose
-// inclusive sum exceeds tau and the exclusive sum before it.
-template <typename MassFn>
-__device__ double chunk_total(int64_t nchunk, int lane, MassFn mass) {
-  double carry = 0.0;
-  for (int64_t base = 0; base < nchunk; base += kWave) {
-    const int64_t c = base + lane;
-    const double v = c < nchunk ? mass(c) : 0.0;
-    const double incl = wave_inclusive_scan(v, lane);
-    carry += wave_broadcast(incl, kWave - 1);
-  }
-  return carry;
-}
-
-template <typename MassFn>
-__device__ int64_t chunk_locate(int64_t nchunk, int lane, double tau, double* before,
-                                MassFn mass) {
-  double carry = 0.0;
-  int64_t last_pos = -1;
-  double last_before = 0.0;
-  for (int64_t base = 0; base < nchunk; base += kWave) {
-    const int64_t c = base + lane;
-    const double v = c < nchunk ? mass(c) : 0.0;
-    const double incl = wave_inclusive_scan(v, lane);
-    const uint64_t hit = __ballot(c < nchunk && carry + incl > tau);
-    if (hit) {
-      const int L = __builtin_ctzll(hit);
-      const double excl = wave_broadcast(incl - v, L);
-      *before = carry + excl;
-      return base + L;
-    }
-    const uint64_t pos = __ballot(c < nchunk && v > 0.0);
-    if (pos) {
-      const int L = 63 - __builtin_clzll(pos);
-      last_before = carry + wave_broadcast(incl - v, L);
-      last_pos = base + L;
-    }
-    carry += wave_broadcast(incl, kWave - 1);
-  }
-  // Not reached for tau < total; kept as a defined fallback (last chunk with mass).
-  *before = last_before;
-  return last_pos < 0 ? 0 : last_pos;
-}
+// ------------------------------------------------------------------------------------ draw
 
 // Scan one chunk in token order and return the first element with positive weight at which
 // the running weight exceeds tau_loc; if rounding leaves tau_loc unreached, the last element
@@ -335,115 +152,383 @@ __device__ int64_t chunk_scan(int64_t c, int64_t V, int lane, double tau_loc, Te
   return first < V ? first : V - 1;
 }
 
+// ------------------------------------------------------------------------------------ finisher
+
+// One wave merges the chunk partials of one row into (M, S, valid): M = max_c m_c and
+// S = sum_c S_c exp((m_c - M)/T) in fp64.  Partials are fetched kMergeBatch per lane at a
+// time, all loads in flight together; rows of up to 64 * kMergeBatch chunks are read once.
+constexpr int kMergeBatch = 4;
+
+__device__ RowStat merge_row(const RowPart* pp, int64_t nchunk, int lane, double Td) {
+  const bool single = nchunk <= int64_t(kWave) * kMergeBatch;
+  RowPart r[kMergeBatch];
+  float mloc = -INFINITY;
+  for (int64_t base = 0; base < nchunk; base += int64_t(kWave) * kMergeBatch) {
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int64_t c = base + i * kWave + lane;
+      r[i] = c < nchunk ? pp[c] : RowPart{-INFINITY, 0, 0.0};
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) mloc = fmaxf(mloc, r[i].m);
+  }
+  const float m = wave_max(mloc);
+  const bool finite_max = (m > -INFINITY) && (m < INFINITY);
+  double s = 0.0;
+  if (finite_max) {
+    for (int64_t base = 0; base < nchunk; base += int64_t(kWave) * kMergeBatch) {
+      if (!single) {
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+          const int64_t c = base + i * kWave + lane;
+          r[i] = c < nchunk ? pp[c] : RowPart{-INFINITY, 0, 0.0};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const double f = r[i].m == -INFINITY ? 0.0 : exp((double(r[i].m) - double(m)) / Td);
+        s += r[i].s * f;  // a NaN partial survives the zero factor
+      }
+    }
+  }
+  s = wave_sum(s);
+  return RowStat{m, finite_max && (s > 0.0) && (s < INFINITY), s};
+}
+
+struct FinishShared {
+  RowStat st[2 * kMaxGamma + 1];
+};
+
+// Sweep finisher: completes the decision for sequence b once every chunk partial of it is in
+// `part`.  Called by all threads of the finishing workgroup.
 template <typename T, int VW>
-__global__ __launch_bounds__(kWave) void k_chain_draw(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ uni,
-    const float* __restrict__ temp, int gamma, int64_t V, int64_t nchunk,
-    const RowPart* __restrict__ part, const RowStat* __restrict__ rowstat,
-    const SeqDecision* __restrict__ seq, const double* __restrict__ wres,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nacc,
-    int32_t* __restrict__ out_status) {
-  const int64_t b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const SeqDecision d = seq[b];
-  if (d.mode == kDrawNone) return;
+__device__ void decide_sequence(const ChainParams& p, int64_t b, FinishShared& sh) {
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const int gamma = p.gamma;
+  const int64_t V = p.V, nchunk = p.nchunk;
   const int R = 2 * gamma + 1;
-  const int k = d.k;
-  int status = d.status;
-  const float tb = temp[b];
-  const float te = effective_temperature(tb);
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float tb = p.temp[b];
+  const double Td = effective_temperature(tb);
+
+  // Row max and normaliser of every row of the sequence, one wave per row.
+  for (int j = wave; j < R; j += kWavesPerBlock) {
+    const RowStat st = merge_row(p.part + (b * R + j) * nchunk, nchunk, lane, Td);
+    if (lane == 0) {
+      sh.st[j] = st;
+      p.rowstat[b * R + j] = st;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  // Accept tests (lane i = position i) and the cut.
+  int status = 0;
+  if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
+  bool bad = false;
+  for (int i = lane; i <= gamma; i += kWave) {
+    const float u = p.uni[b * (gamma + 1) + i];
+    bad |= !(u >= 0.0f && u < 1.0f);
+  }
+  if (__any(bad)) status |= SV_ROW_BAD_UNIFORM;
+  int x = 0;
+  bad = false;
+  if (lane < gamma) {
+    x = p.toks[b * gamma + lane];
+    bad = (x < 0) || (int64_t(x) >= V);
+  }
+  if (__any(bad)) status |= SV_ROW_TOKEN_RANGE;
+  bad = false;
+  for (int j = lane; j < R; j += kWave) bad |= !sh.st[j].valid;
+  if (__any(bad)) status |= SV_ROW_NONFINITE;
+
+  const bool fallback = (status & (SV_ROW_TOKEN_RANGE | SV_ROW_NONFINITE |
+                                   SV_ROW_BAD_TEMPERATURE | SV_ROW_BAD_UNIFORM)) != 0;
+  int k = 0;
+  if (!fallback) {
+    bool accept = false;
+    if (lane < gamma) {
+      const RowStat a = sh.st[lane];
+      const RowStat d = sh.st[gamma + 1 + lane];
+      const double zt = widen(chain_row(tgt, drf, b, gamma, lane, V)[x]);
+      const double zd = widen(chain_row(tgt, drf, b, gamma, gamma + 1 + lane, V)[x]);
+      const double pi = exp((zt - double(a.m)) / Td) / a.s;
+      const double qi = exp((zd - double(d.m)) / Td) / d.s;
+      const double u = p.uni[b * (gamma + 1) + lane];
+      if (qi > 0.0) {
+        accept = u < fmin(1.0, pi / qi);
+      } else {
+        accept = (pi > 0.0) && (u < 1.0);  // ratio +inf; p = q = 0 rejects
+      }
+      if (p.out_p) p.out_p[b * gamma + lane] = float(pi);
+      if (p.out_q) p.out_q[b * gamma + lane] = float(qi);
+    }
+    // k = number of leading ones of the accept mask.
+    const uint64_t rej = ~uint64_t(__ballot(accept && lane < gamma));
+    const int lead = rej == 0 ? kWave : __builtin_ctzll(rej);
+    k = lead < gamma ? lead : gamma;
+  } else if (lane < gamma) {
+    if (p.out_p) p.out_p[b * gamma + lane] = NAN;
+    if (p.out_q) p.out_q[b * gamma + lane] = NAN;
+  }
+  // Accepted prefix and padding; position k is written by the draw kernel.
+  for (int i = lane; i <= gamma; i += kWave) {
+    int32_t v = -1;
+    if (i < k) v = x;  // i < k <= gamma <= 64 only on the first pass, where lane i holds x_i
+    if (fallback && i == 0) v = 0;
+    p.out_tokens[b * (gamma + 1) + i] = v;
+  }
+  if (lane == 0) {
+    p.seq[b] = SeqDecision{k, fallback ? kDrawNone : (k < gamma ? kDrawResidual : kDrawBonus),
+                           status, 0};
+    if (fallback) {
+      p.out_nacc[b] = 0;
+      if (p.out_status) p.out_status[b] = status;
+    }
+  }
+}
+
+// Inverse-CDF step over chunk masses (one wave): total W of the masses in chunk order, then
+// the first chunk whose running sum exceeds u*W, and the running sum before it.  Lane l holds
+// kLocateBatch consecutive chunks of a batch, so rows of up to 64 * kLocateBatch chunks load
+// their masses once, all in flight together.  If rounding leaves u*W unreached, the last chunk
+// with positive mass is returned.
+constexpr int kLocateBatch = 4;
+
+struct Located {
+  int64_t chunk;
+  double before;  // running sum of the masses of the chunks before it
+  double total;
+};
+
+template <typename MassFn>
+__device__ Located locate_chunk(int64_t nchunk, int lane, double u, MassFn mass) {
+  constexpr int NB = kLocateBatch;
+  const int64_t per = int64_t(kWave) * NB;
+  const bool single = nchunk <= per;
+  double v[NB];
+  double carry = 0.0;
+  for (int64_t base = 0; base < nchunk; base += per) {
+    double ls = 0.0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t c = base + int64_t(lane) * NB + i;
+      v[i] = c < nchunk ? mass(c) : 0.0;
+      ls += v[i];
+    }
+    carry += wave_broadcast(wave_inclusive_scan(ls, lane), kWave - 1);
+  }
+  const double total = carry;
+  const double tau = u * total;
+  carry = 0.0;
+  int64_t last_c = -1;
+  double last_before = 0.0;
+  for (int64_t base = 0; base < nchunk; base += per) {
+    double ls = 0.0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t c = base + int64_t(lane) * NB + i;
+      if (!single) v[i] = c < nchunk ? mass(c) : 0.0;
+      ls += v[i];
+    }
+    const double incl = wave_inclusive_scan(ls, lane);
+    double run = carry + (incl - ls);
+    int64_t cand = -1, lp = -1;
+    double cand_before = 0.0, lp_before = 0.0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t c = base + int64_t(lane) * NB + i;
+      const double prev = run;
+      run += v[i];
+      if (v[i] > 0.0) {
+        lp = c;
+        lp_before = prev;
+        if (cand < 0 && run > tau) {
+          cand = c;
+          cand_before = prev;
+        }
+      }
+    }
+    const uint64_t hit = __ballot(cand >= 0);
+    if (hit) {
+      const int L = __builtin_ctzll(hit);
+      return Located{__shfl(cand, L, kWave), wave_broadcast(cand_before, L), total};
+    }
+    const uint64_t pos = __ballot(lp >= 0);
+    if (pos) {
+      const int L = 63 - __builtin_clzll(pos);
+      last_c = __shfl(lp, L, kWave);
+      last_before = wave_broadcast(lp_before, L);
+    }
+    carry += wave_broadcast(incl, kWave - 1);
+  }
+  return Located{last_c < 0 ? 0 : last_c, last_before, total};
+}
+
+// Draw of sequence b (one wave): residual draw over the residual chunk masses (falling back to
+// p_k if they sum to zero), or the bonus draw from p_gamma over the sweep's chunk masses.
+template <typename T, int VW>
+__device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision& d) {
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const int gamma = p.gamma;
+  const int64_t V = p.V, nchunk = p.nchunk;
+  const int R = 2 * gamma + 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float te = effective_temperature(p.temp[b]);
   const double Td = te;
   const float kk = log2e_over_t(te);
-  const double u = uni[b * (gamma + 1) + gamma];
-  const double* wr = wres + b * nchunk;
+  const int k = d.k;
+  int status = d.status;
+  const double u = p.uni[b * (gamma + 1) + gamma];
 
-  bool residual = d.mode == kDrawResidual;
-  if (residual) {
-    const double W = chunk_total(nchunk, lane, [&](int64_t c) { return wr[c]; });
-    if (!(W > 0.0)) {
-      residual = false;
+  int64_t y = -1;
+  if (d.mode == kDrawResidual) {
+    const double* wr = p.wres + b * nchunk;
+    const Located at = locate_chunk(nchunk, lane, u, [&](int64_t c) { return wr[c]; });
+    if (at.total > 0.0) {
+      const int64_t cs = at.chunk;
+      const int jt = k, jd = gamma + 1 + k;
+      const RowPart pt = p.part[(b * R + jt) * nchunk + cs];
+      const RowPart pd = p.part[(b * R + jd) * nchunk + cs];
+      const double A = chunk_scale(pt.m, p.rowstat[b * R + jt], Td);
+      const double Bq = chunk_scale(pd.m, p.rowstat[b * R + jd], Td);
+      float zt[kElemsPerLane], zd[kElemsPerLane];
+      load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jt, V), V, cs, lane, zt);
+      load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jd, V), V, cs, lane, zd);
+      y = chunk_scan<VW>(cs, V, lane, u * at.total - at.before, [&](int i) {
+        return residual_term(zt[i], zd[i], pt.m, pd.m, kk, A, Bq);
+      });
+    } else {
       status |= SV_ROW_RESIDUAL_ZERO;
     }
   }
-
-  int64_t y;
-  if (residual) {
-    auto mass = [&](int64_t c) { return wr[c]; };
-    const double W = chunk_total(nchunk, lane, mass);
-    double before = 0.0;
-    const int64_t cs = chunk_locate(nchunk, lane, u * W, &before, mass);
-    const int jt = k, jd = gamma + 1 + k;
-    const RowPart pt = part[(b * R + jt) * nchunk + cs];
-    const RowPart pd = part[(b * R + jd) * nchunk + cs];
-    const double A = chunk_scale(pt.m, rowstat[b * R + jt], Td);
-    const double Bq = chunk_scale(pd.m, rowstat[b * R + jd], Td);
-    float zt[kElemsPerLane], zd[kElemsPerLane];
-    load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jt, V), V, cs, lane, zt);
-    load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jd, V), V, cs, lane, zd);
-    y = chunk_scan<VW>(cs, V, lane, u * W - before, [&](int i) {
-      return residual_term(zt[i], zd[i], pt.m, pd.m, kk, A, Bq);
-    });
-  } else {
+  if (y < 0) {
     // Bonus draw from p_gamma, or the zero-residual fallback from p_k.
     const int jr = d.mode == kDrawBonus ? gamma : k;
-    const RowStat srow = rowstat[b * R + jr];
-    const RowPart* pp = part + (b * R + jr) * nchunk;
-    auto mass = [&](int64_t c) {
+    const RowStat srow = p.rowstat[b * R + jr];
+    const RowPart* pp = p.part + (b * R + jr) * nchunk;
+    const Located at = locate_chunk(nchunk, lane, u, [&](int64_t c) {
       const RowPart q = pp[c];
       return q.s * chunk_scale(q.m, srow, Td);
-    };
-    const double W = chunk_total(nchunk, lane, mass);
-    double before = 0.0;
-    const double tau = u * W;
-    const int64_t cs = chunk_locate(nchunk, lane, tau, &before, mass);
+    });
+    const int64_t cs = at.chunk;
     const RowPart pc = pp[cs];
     const double scale = chunk_scale(pc.m, srow, Td);
     float z[kElemsPerLane];
     load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jr, V), V, cs, lane, z);
-    const double tau_loc = scale > 0.0 ? (tau - before) / scale : 0.0;
+    const double tau_loc = scale > 0.0 ? (u * at.total - at.before) / scale : 0.0;
     y = chunk_scan<VW>(cs, V, lane, tau_loc,
                        [&](int i) { return double(softmax_term(z[i], pc.m, kk)); });
   }
   if (lane == 0) {
-    out_tokens[b * (gamma + 1) + k] = int32_t(y);
-    out_nacc[b] = k;
-    if (out_status) out_status[b] = status;
+    p.out_tokens[b * (gamma + 1) + k] = int32_t(y);
+    p.out_nacc[b] = k;
+    if (p.out_status) p.out_status[b] = status;
   }
+}
+
+// ------------------------------------------------------------------------------------ kernels
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kBlock) void k_chain_sweep(ChainParams p, int64_t total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
+  if (w >= total) return;  // wave-uniform
+  const int R = 2 * p.gamma + 1;
+  const int64_t row = w / p.nchunk;  // b * R + j
+  const int64_t c = w - row * p.nchunk;
+  const int64_t b = row / R;
+  const int j = int(row - b * R);
+  const float k = log2e_over_t(effective_temperature(p.temp[b]));
+  const T* rp = chain_row(static_cast<const T*>(p.tgt), static_cast<const T*>(p.drf), b, p.gamma,
+                          j, p.V);
+  const RowPart part = sweep_chunk<T, VW>(rp, p.V, c, lane, k);
+  if (lane == 0) p.part[w] = part;
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kBlock) void k_chain_decide(ChainParams p) {
+  __shared__ FinishShared sh;
+  decide_sequence<T, VW>(p, blockIdx.x, sh);
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p, int64_t total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t w = int64_t(blockIdx.x) * (kResidualBlock / kWave) + threadIdx.x / kWave;
+  if (w >= total) return;  // wave-uniform
+  const int64_t b = w / p.nchunk;
+  const int64_t c = w - b * p.nchunk;
+  const SeqDecision d = p.seq[b];
+  if (d.mode != kDrawResidual) return;
+  const int R = 2 * p.gamma + 1;
+  const int jt = d.k, jd = p.gamma + 1 + d.k;
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const float te = effective_temperature(p.temp[b]);
+  const double Td = te;
+  const float kk = log2e_over_t(te);
+  const RowPart pt = p.part[(b * R + jt) * p.nchunk + c];
+  const RowPart pd = p.part[(b * R + jd) * p.nchunk + c];
+  const double A = chunk_scale(pt.m, p.rowstat[b * R + jt], Td);
+  const double Bq = chunk_scale(pd.m, p.rowstat[b * R + jd], Td);
+  float zt[kElemsPerLane], zd[kElemsPerLane];
+  load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jt, p.V), p.V, c, lane, zt);
+  load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jd, p.V), p.V, c, lane, zd);
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < kElemsPerLane; ++i)
+    acc[i & 3] += residual_term(zt[i], zd[i], pt.m, pd.m, kk, A, Bq);
+  const double s = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  if (lane == 0) p.wres[w] = s;
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kWave) void k_chain_draw(ChainParams p) {
+  const int64_t b = blockIdx.x;
+  const SeqDecision d = p.seq[b];
+  if (d.mode == kDrawNone) return;  // fallback: the decide kernel wrote the result
+  draw_sequence<T, VW>(p, b, d);
 }
 
 template <typename T, int VW>
 hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   const ChainLayout L = chain_layout(a.B, a.gamma, a.V);
-  RowPart* part = reinterpret_cast<RowPart*>(a.ws + L.off_part);
-  RowStat* rowstat = reinterpret_cast<RowStat*>(a.ws + L.off_rowstat);
-  SeqDecision* seq = reinterpret_cast<SeqDecision*>(a.ws + L.off_seq);
-  double* wres = reinterpret_cast<double*>(a.ws + L.off_wres);
-  const T* tgt = static_cast<const T*>(a.target);
-  const T* drf = static_cast<const T*>(a.draft);
-  const int64_t rows = int64_t(a.B) * (2 * a.gamma + 1);
-  const int64_t total = rows * L.nchunk;
+  ChainParams p;
+  p.tgt = a.target;
+  p.drf = a.draft;
+  p.toks = a.draft_tokens;
+  p.uni = a.uniforms;
+  p.temp = a.temperature;
+  p.gamma = a.gamma;
+  p.V = a.V;
+  p.nchunk = L.nchunk;
+  p.part = reinterpret_cast<RowPart*>(a.ws + L.off_part);
+  p.rowstat = reinterpret_cast<RowStat*>(a.ws + L.off_rowstat);
+  p.seq = reinterpret_cast<SeqDecision*>(a.ws + L.off_seq);
+  p.wres = reinterpret_cast<double*>(a.ws + L.off_wres);
+  p.out_tokens = a.out_tokens;
+  p.out_nacc = a.out_num_accepted;
+  p.out_p = a.out_p;
+  p.out_q = a.out_q;
+  p.out_status = a.out_status;
 
-  hipError_t e = launch_kernel("chain_rowstats", k_chain_rowstats<T, VW>,
+  const int64_t total = int64_t(a.B) * (2 * a.gamma + 1) * L.nchunk;
+  hipError_t e = launch_kernel("chain_sweep", k_chain_sweep<T, VW>,
                                dim3(unsigned((total + kWavesPerBlock - 1) / kWavesPerBlock)),
-                               dim3(kBlock), s, tgt, drf, a.temperature, a.gamma, a.V, L.nchunk,
-                               total, part);
+                               dim3(kBlock), s, p, total);
   if (e != hipSuccess) return e;
-  e = launch_kernel("chain_decide", k_chain_decide<T>, dim3(unsigned(a.B)), dim3(kBlock), s, tgt, drf,
-                    a.draft_tokens, a.uniforms, a.temperature, a.gamma, a.V, L.nchunk,
-                    (const RowPart*)part, rowstat, seq, a.out_tokens, a.out_num_accepted,
-                    a.out_p, a.out_q, a.out_status);
+  e = launch_kernel("chain_decide", k_chain_decide<T, VW>, dim3(unsigned(a.B)), dim3(kBlock), s, p);
   if (e != hipSuccess) return e;
   const int64_t rtotal = int64_t(a.B) * L.nchunk;
+  constexpr int rw = kResidualBlock / kWave;
   e = launch_kernel("chain_residual", k_chain_residual<T, VW>,
-                    dim3(unsigned((rtotal + kWavesPerBlock - 1) / kWavesPerBlock)),
-                    dim3(kBlock), s, tgt, drf, a.temperature, a.gamma, a.V, L.nchunk, rtotal,
-                    (const RowPart*)part, (const RowStat*)rowstat, (const SeqDecision*)seq,
-                    wres);
+                    dim3(unsigned((rtotal + rw - 1) / rw)), dim3(kResidualBlock), s, p, rtotal);
   if (e != hipSuccess) return e;
-  return launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s, tgt, drf,
-                       a.uniforms, a.temperature, a.gamma, a.V, L.nchunk, (const RowPart*)part,
-                       (const RowStat*)rowstat, (const SeqDecision*)seq, (const double*)wres,
-                       a.out_tokens, a.out_num_accepted, a.out_status);
+  return launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s, p);
 }
 
 }  // namespace

@@ -66,15 +66,16 @@ __device__ __forceinline__ int chunk_offset(int j, int lane, int t) {
   return (j * kWave + lane) * VW + t;
 }
 
-template <typename T, int VW>
-__device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t V, int64_t c, int lane,
-                                           float (&z)[kElemsPerLane]) {
-  constexpr int NLD = kElemsPerLane / VW;
+// Loads j in [J0, J0 + NJ) of the lane's share of chunk c into z[0 .. NJ*VW); z[(j-J0)*VW + t]
+// holds element (j, t).
+template <typename T, int VW, int J0, int NJ>
+__device__ __forceinline__ void load_chunk_part(const T* __restrict__ row, int64_t V, int64_t c,
+                                                int lane, float (&z)[NJ * VW]) {
   const int64_t c0 = c * kChunk;
   if constexpr (VW == 1) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int64_t e = c0 + j * kWave + lane;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t e = c0 + (J0 + j) * kWave + lane;
       z[j] = e < V ? widen(row[e]) : -INFINITY;
     }
   } else {
@@ -82,15 +83,15 @@ __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t V,
     const VT* vrow = reinterpret_cast<const VT*>(row);
     const int64_t nvec = V / VW;
     const int64_t v0 = c0 / VW;
-    VT buf[NLD];
+    VT buf[NJ];
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int64_t vi = v0 + j * kWave + lane;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t vi = v0 + (J0 + j) * kWave + lane;
       if (vi < nvec) buf[j] = vrow[vi];
     }
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int64_t vi = v0 + j * kWave + lane;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t vi = v0 + (J0 + j) * kWave + lane;
       if (vi < nvec) {
         unpack<T, VW>(buf[j], &z[j * VW]);
       } else {
@@ -99,6 +100,12 @@ __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t V,
       }
     }
   }
+}
+
+template <typename T, int VW>
+__device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t V, int64_t c, int lane,
+                                           float (&z)[kElemsPerLane]) {
+  load_chunk_part<T, VW, 0, kElemsPerLane / VW>(row, V, c, lane, z);
 }
 
 // ---------------------------------------------------------------------------- wave collectives
@@ -139,6 +146,68 @@ __device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
 }
 
 __device__ __forceinline__ double wave_broadcast(double v, int src) { return __shfl(v, src, kWave); }
+
+// ---------------------------------------------------------------------------- cross-workgroup records
+//
+// Small per-chunk records written by one workgroup and read by another (possibly on another
+// XCD, whose L2 is not coherent with the writer's).  Both sides use device-scope relaxed
+// atomic accesses, which carry device coherence on the instruction itself, so no cache-wide
+// maintenance (an agent-scope fence writes back and invalidates the whole L2) is needed.
+// The writer waits for its stores to complete (s_waitcnt 0) before the workgroup barrier
+// that precedes its completion count; a reader reads only after observing the final count.
+
+__device__ __forceinline__ void store_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t load_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int32_t count_dev(int32_t* p) {
+  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ uint64_t pack2(uint32_t lo, uint32_t hi) {
+  return uint64_t(lo) | (uint64_t(hi) << 32);
+}
+
+__device__ __forceinline__ void publish(RowPart* dst, const RowPart& v) {
+  uint64_t* w = reinterpret_cast<uint64_t*>(dst);
+  store_dev(w, pack2(__float_as_uint(v.m), uint32_t(v.pad)));
+  store_dev(w + 1, uint64_t(__double_as_longlong(v.s)));
+}
+
+__device__ __forceinline__ RowPart fetch(const RowPart* src) {
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(src);
+  const uint64_t a = load_dev(w), b = load_dev(w + 1);
+  return RowPart{__uint_as_float(uint32_t(a)), int32_t(a >> 32), __longlong_as_double(int64_t(b))};
+}
+
+__device__ __forceinline__ void publish(ArgPart* dst, const ArgPart& v) {
+  uint64_t* w = reinterpret_cast<uint64_t*>(dst);
+  store_dev(w, pack2(__float_as_uint(v.v), uint32_t(v.idx)));
+  store_dev(w + 1, pack2(uint32_t(v.nan), uint32_t(v.pad)));
+}
+
+__device__ __forceinline__ ArgPart fetch(const ArgPart* src) {
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(src);
+  const uint64_t a = load_dev(w), b = load_dev(w + 1);
+  return ArgPart{__uint_as_float(uint32_t(a)), int32_t(a >> 32), int32_t(uint32_t(b)),
+                 int32_t(b >> 32)};
+}
+
+// Logical workgroup index for an XCD-aware layout: hardware workgroup i runs on XCD
+// i % kXcds, so XCD x receives i = x, x + kXcds, ...; it is given the x-th contiguous block of
+// logical indices, in order.  A bijection on [0, n) for any n.
+__device__ __forceinline__ int64_t xcd_logical_index(int64_t i, int64_t n) {
+  const int64_t x = i % kXcds, r = i / kXcds;
+  const int64_t full = n / kXcds, rem = n % kXcds;
+  return x * full + (x < rem ? x : rem) + r;
+}
 
 // 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

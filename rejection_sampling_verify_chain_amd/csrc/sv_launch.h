@@ -16,8 +16,8 @@ void trace_before(const char* name, hipStream_t stream);
 void trace_after(hipStream_t stream);
 
 template <typename... KArgs, typename... Args>
-hipError_t launch_kernel(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block,
-                         hipStream_t stream, Args&&... args) {
+hipError_t launch_kernel_shm(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                             size_t shared_bytes, hipStream_t stream, Args&&... args) {
   static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
   std::tuple<KArgs...> held(static_cast<KArgs>(std::forward<Args>(args))...);
   void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
@@ -30,9 +30,16 @@ hipError_t launch_kernel(const char* name, void (*kernel)(KArgs...), dim3 grid, 
   const bool tr = trace_on();
   if (tr) trace_before(name, stream);
   const hipError_t err =
-      hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
+      hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shared_bytes,
+                      stream);
   if (tr) trace_after(stream);
   return err;
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                         hipStream_t stream, Args&&... args) {
+  return launch_kernel_shm(name, kernel, grid, block, 0, stream, std::forward<Args>(args)...);
 }
 
 }  // namespace sv

@@ -6,14 +6,16 @@
 // that node; verification walks from the root along children whose token equals
 // that output and appends the agreeing run.  Greedy outputs are per-node argmaxes.
 //
-// Pipeline:
-//   1. argmax  one wave per (node row, chunk): chunk maximum over non-NaN entries and
-//              the lowest index attaining it.  The single HBM sweep over all logits.
-//   2. walk    one workgroup per tree: merge chunk partials into g[u] for every node,
-//              validate the parent array, then one wave walks from the root: at node u
-//              a ballot over the nodes finds the lowest-id child c with parent u and
-//              token g[u]; the accepted path and tokens are written, then g of the last
-//              accepted node as the bonus token.
+// Two launches per call:
+//   init    zeroes one completion counter per tree.
+//   verify  the single HBM sweep: workgroups are laid out tree by tree, each of the 16 waves
+//           of a workgroup owns one chunk (2048 elements) of one node's logit row and writes
+//           the chunk maximum over non-NaN entries and the lowest index attaining it.  The
+//           last workgroup of a tree to finish merges the partials into g[u] for every
+//           node, validates the parent array, and walks from the root with one wave: at
+//           node u a ballot over the nodes finds the lowest-id child c with parent u and
+//           token g[u]; it writes the accepted path and tokens, then g of the last accepted
+//           node as the bonus token.
 
 #include <math.h>
 
@@ -24,22 +26,33 @@
 namespace sv {
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = 1024;
 constexpr int kWavesPerBlock = kBlock / kWave;
+static_assert(kWavesPerBlock == kChunksPerGroup, "one chunk per wave");
 
+struct TreeParams {
+  const void* logits;
+  const int32_t* parents;
+  const int32_t* node_tokens;
+  int n_nodes;
+  int wg_per_tree;
+  int64_t V;
+  int64_t nchunk;
+  ArgPart* part;
+  int32_t* counter;
+  int32_t* out_path;
+  int32_t* out_tokens;
+  int32_t* out_nacc;
+  int32_t* out_g;
+  int32_t* out_status;
+};
+
+// One wave: chunk c of a logit row -> (max over non-NaN entries, lowest index holding it).
 template <typename T, int VW>
-__global__ __launch_bounds__(kBlock) void k_tree_argmax(const T* __restrict__ logits, int64_t V,
-                                                        int64_t nchunk, int64_t total,
-                                                        ArgPart* __restrict__ part) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x / kWave);
-  if (w >= total) return;
-  const int64_t row = w / nchunk;
-  const int64_t c = w - row * nchunk;
-
+__device__ __forceinline__ ArgPart argmax_chunk(const T* __restrict__ row, int64_t V, int64_t c,
+                                                int lane) {
   float z[kElemsPerLane];
-  load_chunk<T, VW>(logits + row * V, V, c, lane, z);
-
+  load_chunk<T, VW>(row, V, c, lane, z);
   float m = -INFINITY;
   bool nan = false;
 #pragma unroll
@@ -60,65 +73,103 @@ __global__ __launch_bounds__(kBlock) void k_tree_argmax(const T* __restrict__ lo
   }
   idx = wave_min(idx);
   const int any_nan = __any(nan);
-  if (lane == 0) {
-    part[w] = ArgPart{m, idx == INT32_MAX ? INT32_MAX : int32_t(c * kChunk + idx), any_nan, 0};
-  }
+  return ArgPart{m, idx == INT32_MAX ? INT32_MAX : int32_t(c * kChunk + idx), any_nan, 0};
 }
 
-__global__ __launch_bounds__(kBlock) void k_tree_walk(
-    const int32_t* __restrict__ parents, const int32_t* __restrict__ node_tokens, int n_nodes,
-    int64_t V, int64_t nchunk, const ArgPart* __restrict__ part, int32_t* __restrict__ out_path,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nacc,
-    int32_t* __restrict__ out_g, int32_t* __restrict__ out_status) {
-  __shared__ int32_t g[kMaxTreeNodes];
-  __shared__ int32_t par[kMaxTreeNodes];
-  __shared__ int32_t tok[kMaxTreeNodes];
-  __shared__ int32_t flags;
-  const int64_t t = blockIdx.x;
-  const int64_t base = t * n_nodes;
-  if (threadIdx.x == 0) flags = 0;
-  __syncthreads();
+// Walk state in LDS, sized by the launch to 3 * n_nodes words: argmax, parent and token of
+// every node.  Only the finishing workgroup of a tree touches it.
+struct WalkShared {
+  int32_t* g;
+  int32_t* par;
+  int32_t* tok;
+  int32_t flags;
+};
 
-  int local = 0;
-  for (int u = threadIdx.x; u < n_nodes; u += kBlock) {
-    const ArgPart* pp = part + (base + u) * nchunk;
-    float best = -INFINITY;
-    int32_t bidx = INT32_MAX;
-    int nan = 0;
-    for (int64_t c = 0; c < nchunk; ++c) {
-      const ArgPart a = pp[c];
-      if (a.v > best || (a.v == best && a.idx < bidx)) {
-        best = a.v;
-        bidx = a.idx;
-      }
-      nan |= a.nan;
+// (value, index) order of the argmax: larger value first, then lower index.
+__device__ __forceinline__ bool arg_better(float v, int32_t i, float bv, int32_t bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// One wave merges the chunk partials of one node row: the row's argmax (lowest index among
+// equal maxima) and whether the row holds a NaN.  Lanes take chunks, all loads of a batch in
+// flight together, then a butterfly reduction with the argmax order.
+constexpr int kMergeBatch = 4;
+
+__device__ void merge_node(const ArgPart* pp, int64_t nchunk, int lane, int32_t* g, int* nan) {
+  float best = -INFINITY;
+  int32_t bidx = INT32_MAX;
+  int anynan = 0;
+  for (int64_t base = 0; base < nchunk; base += int64_t(kWave) * kMergeBatch) {
+    ArgPart r[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int64_t c = base + i * kWave + lane;
+      r[i] = c < nchunk ? fetch(&pp[c]) : ArgPart{-INFINITY, INT32_MAX, 0, 0};
     }
-    const int32_t gu = bidx == INT32_MAX ? 0 : bidx;
-    const int32_t pu = parents[base + u];
-    const int32_t tu = node_tokens[base + u];
-    g[u] = gu;
-    par[u] = pu;
-    tok[u] = tu;
-    if (out_g) out_g[base + u] = gu;
-    if (nan) local |= SV_ROW_NONFINITE;
-    if (u == 0 ? pu != -1 : (pu < 0 || pu >= u)) local |= SV_ROW_BAD_TREE;
-    if (u > 0 && (tu < 0 || int64_t(tu) >= V)) local |= SV_ROW_TOKEN_RANGE;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (arg_better(r[i].v, r[i].idx, best, bidx)) {
+        best = r[i].v;
+        bidx = r[i].idx;
+      }
+      anynan |= r[i].nan;
+    }
   }
-  if (local) atomicOr(&flags, local);
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, kWave);
+    const int32_t oi = __shfl_xor(bidx, o, kWave);
+    if (arg_better(ov, oi, best, bidx)) {
+      best = ov;
+      bidx = oi;
+    }
+  }
+  *g = bidx == INT32_MAX ? 0 : bidx;
+  *nan = __any(anynan);
+}
+
+// Completes tree t once every chunk partial of it is in `part` (all threads of the group).
+__device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
+  const int n_nodes = p.n_nodes;
+  const int64_t base = t * n_nodes;
+  const int64_t nchunk = p.nchunk;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (threadIdx.x == 0) sh.flags = 0;
+  __syncthreads();
+  int local = 0;
+  for (int u = wave; u < n_nodes; u += kWavesPerBlock) {
+    int32_t gu;
+    int nan;
+    merge_node(p.part + (base + u) * nchunk, nchunk, lane, &gu, &nan);
+    if (lane == 0) {
+      sh.g[u] = gu;
+      if (p.out_g) p.out_g[base + u] = gu;
+      if (nan) local |= SV_ROW_NONFINITE;
+    }
+  }
+  for (int u = threadIdx.x; u < n_nodes; u += kBlock) {
+    const int32_t pu = p.parents[base + u];
+    const int32_t tu = p.node_tokens[base + u];
+    sh.par[u] = pu;
+    sh.tok[u] = tu;
+    if (u == 0 ? pu != -1 : (pu < 0 || pu >= u)) local |= SV_ROW_BAD_TREE;
+    if (u > 0 && (tu < 0 || int64_t(tu) >= p.V)) local |= SV_ROW_TOKEN_RANGE;
+  }
+  if (local) atomicOr(&sh.flags, local);
   __syncthreads();
   if (threadIdx.x >= kWave) return;
-  const int lane = threadIdx.x;
-  const int status = flags;
+  const int status = sh.flags;
 
   int k = 0;
   int u = 0;
   if (!(status & (SV_ROW_BAD_TREE | SV_ROW_TOKEN_RANGE))) {
     for (;;) {
-      const int32_t want = g[u];
+      const int32_t want = sh.g[u];
       int found = -1;
       for (int b0 = 0; b0 < n_nodes; b0 += kWave) {
         const int i = b0 + lane;
-        const bool m = i > 0 && i < n_nodes && par[i] == u && tok[i] == want;
+        const bool m = i > 0 && i < n_nodes && sh.par[i] == u && sh.tok[i] == want;
         const uint64_t hit = __ballot(m);
         if (hit) {
           found = b0 + __builtin_ctzll(hit);
@@ -128,37 +179,85 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(
       if (found < 0) break;  // parents precede children, so the walk ends within n_nodes steps
       ++k;
       if (lane == 0) {
-        out_path[base + k] = found;
-        out_tokens[base + k - 1] = tok[found];
+        p.out_path[base + k] = found;
+        p.out_tokens[base + k - 1] = sh.tok[found];
       }
       u = found;
     }
   }
   for (int i = lane; i < n_nodes; i += kWave) {
-    if (i == 0) out_path[base] = 0;
-    if (i > k) out_path[base + i] = -1;
-    if (i == k) out_tokens[base + i] = g[u];
-    if (i > k) out_tokens[base + i] = -1;
+    if (i == 0) p.out_path[base] = 0;
+    if (i > k) p.out_path[base + i] = -1;
+    if (i == k) p.out_tokens[base + i] = sh.g[u];
+    if (i > k) p.out_tokens[base + i] = -1;
   }
   if (lane == 0) {
-    out_nacc[t] = k;
-    if (out_status) out_status[t] = status;
+    p.out_nacc[t] = k;
+    if (p.out_status) p.out_status[t] = status;
   }
+}
+
+__global__ __launch_bounds__(256) void k_tree_init(int32_t* __restrict__ counter, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) counter[i * kCounterStride] = 0;
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8))) void k_tree_verify(TreeParams p) {
+  extern __shared__ int32_t walk_lds[];
+  __shared__ WalkShared sh;
+  __shared__ int32_t is_last;
+  const int64_t lg = xcd_logical_index(blockIdx.x, gridDim.x);  // one tree range per XCD
+  const int64_t t = lg / p.wg_per_tree;
+  const int64_t g = lg - t * p.wg_per_tree;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t idx = g * kWavesPerBlock + wave;  // chunk index within the tree
+  if (idx < p.n_nodes * p.nchunk) {               // wave-uniform
+    const int64_t u = idx / p.nchunk;
+    const int64_t c = idx - u * p.nchunk;
+    const T* row = static_cast<const T*>(p.logits) + (t * p.n_nodes + u) * p.V;
+    const ArgPart a = argmax_chunk<T, VW>(row, p.V, c, lane);
+    if (lane == 0) publish(&p.part[(t * p.n_nodes + u) * p.nchunk + c], a);
+  }
+  // Partials are complete before the workgroup is counted; the last one finishes the tree.
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = count_dev(&p.counter[t * kCounterStride]) == p.wg_per_tree - 1;
+  __syncthreads();
+  if (!is_last) return;
+  if (threadIdx.x == 0) {
+    sh.g = walk_lds;
+    sh.par = walk_lds + p.n_nodes;
+    sh.tok = walk_lds + 2 * p.n_nodes;
+  }
+  finish_tree(p, t, sh);
 }
 
 template <typename T, int VW>
 hipError_t run_tree(const TreeArgs& a, hipStream_t s) {
   const TreeLayout L = tree_layout(a.n_trees, a.n_nodes, a.V);
-  ArgPart* part = reinterpret_cast<ArgPart*>(a.ws + L.off_part);
-  const int64_t total = int64_t(a.n_trees) * a.n_nodes * L.nchunk;
-  hipError_t e = launch_kernel("tree_argmax", k_tree_argmax<T, VW>,
-                               dim3(unsigned((total + kWavesPerBlock - 1) / kWavesPerBlock)),
-                               dim3(kBlock), s, static_cast<const T*>(a.logits), a.V, L.nchunk,
-                               total, part);
+  TreeParams p;
+  p.logits = a.logits;
+  p.parents = a.parents;
+  p.node_tokens = a.node_tokens;
+  p.n_nodes = a.n_nodes;
+  p.wg_per_tree = int(groups_per_unit(a.n_nodes, a.V));
+  p.V = a.V;
+  p.nchunk = L.nchunk;
+  p.part = reinterpret_cast<ArgPart*>(a.ws + L.off_part);
+  p.counter = reinterpret_cast<int32_t*>(a.ws + L.off_counter);
+  p.out_path = a.out_path;
+  p.out_tokens = a.out_tokens;
+  p.out_nacc = a.out_num_accepted;
+  p.out_g = a.out_node_argmax;
+  p.out_status = a.out_status;
+  hipError_t e = launch_kernel("tree_init", k_tree_init, dim3(unsigned((a.n_trees + 255) / 256)),
+                               dim3(256), s, p.counter, int64_t(a.n_trees));
   if (e != hipSuccess) return e;
-  return launch_kernel("tree_walk", k_tree_walk, dim3(unsigned(a.n_trees)), dim3(kBlock), s, a.parents,
-                       a.node_tokens, a.n_nodes, a.V, L.nchunk, (const ArgPart*)part, a.out_path,
-                       a.out_tokens, a.out_num_accepted, a.out_node_argmax, a.out_status);
+  return launch_kernel_shm("tree_verify", k_tree_verify<T, VW>,
+                           dim3(unsigned(int64_t(a.n_trees) * p.wg_per_tree)), dim3(kBlock),
+                           size_t(3) * sizeof(int32_t) * size_t(a.n_nodes), s, p);
 }
 
 }  // namespace
