@@ -18,8 +18,8 @@ int vec_width(sv_dtype dtype) { return dtype == SV_F32 ? 4 : 8; }
 
 bool valid_dtype(sv_dtype dtype) { return dtype == SV_F32 || dtype == SV_BF16; }
 
-// Grid sizes are 32-bit: `units` sequences (or trees) of `rows` logit rows each, one
-// workgroup per four (row, chunk) pairs of a unit.
+// Grid sizes are 32-bit: `units` sequences (or trees) of `rows` logit rows each, one wave per
+// (row, chunk) pair and at least four waves per workgroup.
 bool grid_fits(int64_t units, int64_t rows, int64_t V) {
   return units * sv::groups_per_unit(rows, V) < int64_t(INT32_MAX);
 }
@@ -27,7 +27,7 @@ bool grid_fits(int64_t units, int64_t rows, int64_t V) {
 bool chain_shape_ok(int32_t B, int32_t gamma, int64_t V) {
   if (B < 1 || B > sv::kMaxBatch || gamma < 1 || gamma > sv::kMaxGamma) return false;
   if (V < 1 || V > int64_t(INT32_MAX)) return false;
-  return grid_fits(B, 2 * gamma + 1, V);  // the draw grid (one row per sequence) is smaller
+  return grid_fits(B, 2 * gamma + 1, V);
 }
 
 bool tree_shape_ok(int32_t n_trees, int32_t n_nodes, int64_t V) {

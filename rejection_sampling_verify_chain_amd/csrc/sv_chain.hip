@@ -21,6 +21,10 @@
 //   draw      one wave per sequence draws y by inverse CDF: a running sum over the chunk
 //             masses (the residual masses, or the bonus row's p masses from the sweep) locates
 //             the chunk holding u*W, and that chunk is rescanned in token order.
+// Fusing the per-sequence tails into the streaming kernels (a last-workgroup finisher) was
+// measured slower: the finisher's registers lower the streaming kernel's occupancy, its
+// latency-bound work stretches under a saturated memory system, and it lands on whichever
+// XCD lags.
 
 #include <math.h>
 
@@ -33,8 +37,7 @@ namespace {
 
 constexpr int kBlock = 1024;  // sweep and decide
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kResidualBlock = 256;
-static_assert(kWavesPerBlock == kChunksPerGroup, "one chunk per wave");
+constexpr int kResidualBlock = 256;  // residual: one chunk per wave
 
 struct ChainParams {
   const void* tgt;
@@ -75,13 +78,28 @@ __device__ __forceinline__ double chunk_scale(float mc, const RowStat& st, doubl
   return exp((double(mc) - double(st.m)) / Td) / st.s;
 }
 
-// Residual weight max(0, p(x) - q(x)) at one token, from the chunk-local terms.
-__device__ __forceinline__ double residual_term(float zt, float zd, float mt, float md, float k,
-                                                double A, double Bq) {
-  const double pt = A > 0.0 ? double(softmax_term(zt, mt, k)) * A : 0.0;
-  const double qd = Bq > 0.0 ? double(softmax_term(zd, md, k)) * Bq : 0.0;
-  const double d = pt - qd;
-  return d > 0.0 ? d : 0.0;
+// Residual weights of one chunk, max(0, p(x) - q(x)) = A * max(0, e_t(x) - lambda * e_d(x)):
+// e_t, e_d are the chunk-local softmax terms of target and draft row k, A = exp((m_t,c - M_t)/T)
+// / S_t scales e_t to p, and lambda = B / A with B the draft's scale.  Per element this is one
+// fp32 FMA (the product is exact inside it, so the difference rounds once) and a max; A is
+// applied per chunk in fp64.  A = 0 (target chunk all -inf) gives no residual mass; B = 0
+// (draft chunk all -inf) gives lambda = 0 and e_d is not formed.
+struct ResidualScale {
+  double A;
+  float lambda;
+  bool qlive;
+};
+
+__device__ __forceinline__ ResidualScale residual_scale(double A, double Bq) {
+  if (!(A > 0.0)) return ResidualScale{0.0, 0.0f, false};
+  return ResidualScale{A, float(fmin(Bq / A, 3.40282347e38)), Bq > 0.0};
+}
+
+__device__ __forceinline__ float residual_term(float zt, float zd, float mt, float md, float k,
+                                               const ResidualScale& rs) {
+  const float et = softmax_term(zt, mt, k);
+  const float ed = rs.qlive ? softmax_term(zd, md, k) : 0.0f;
+  return fmaxf(0.0f, fmaf(-rs.lambda, ed, et));
 }
 
 // ------------------------------------------------------------------------------------ sweep
@@ -152,7 +170,7 @@ __device__ int64_t chunk_scan(int64_t c, int64_t V, int lane, double tau_loc, Te
   return first < V ? first : V - 1;
 }
 
-// ------------------------------------------------------------------------------------ finisher
+// -------------------------------------------------------------------------------------- decide
 
 // One wave merges the chunk partials of one row into (M, S, valid): M = max_c m_c and
 // S = sum_c S_c exp((m_c - M)/T) in fp64.  Partials are fetched kMergeBatch per lane at a
@@ -195,14 +213,14 @@ __device__ RowStat merge_row(const RowPart* pp, int64_t nchunk, int lane, double
   return RowStat{m, finite_max && (s > 0.0) && (s < INFINITY), s};
 }
 
-struct FinishShared {
+struct DecideShared {
   RowStat st[2 * kMaxGamma + 1];
 };
 
-// Sweep finisher: completes the decision for sequence b once every chunk partial of it is in
-// `part`.  Called by all threads of the finishing workgroup.
+// The decision for sequence b from the chunk partials of its rows.  Called by all threads of
+// the sequence's workgroup.
 template <typename T, int VW>
-__device__ void decide_sequence(const ChainParams& p, int64_t b, FinishShared& sh) {
+__device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& sh) {
   const T* tgt = static_cast<const T*>(p.tgt);
   const T* drf = static_cast<const T*>(p.drf);
   const int gamma = p.gamma;
@@ -393,13 +411,14 @@ __device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision
       const int jt = k, jd = gamma + 1 + k;
       const RowPart pt = p.part[(b * R + jt) * nchunk + cs];
       const RowPart pd = p.part[(b * R + jd) * nchunk + cs];
-      const double A = chunk_scale(pt.m, p.rowstat[b * R + jt], Td);
-      const double Bq = chunk_scale(pd.m, p.rowstat[b * R + jd], Td);
+      const ResidualScale rs = residual_scale(chunk_scale(pt.m, p.rowstat[b * R + jt], Td),
+                                              chunk_scale(pd.m, p.rowstat[b * R + jd], Td));
       float zt[kElemsPerLane], zd[kElemsPerLane];
       load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jt, V), V, cs, lane, zt);
       load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jd, V), V, cs, lane, zd);
-      y = chunk_scan<VW>(cs, V, lane, u * at.total - at.before, [&](int i) {
-        return residual_term(zt[i], zd[i], pt.m, pd.m, kk, A, Bq);
+      const double tau_loc = rs.A > 0.0 ? (u * at.total - at.before) / rs.A : 0.0;
+      y = chunk_scan<VW>(cs, V, lane, tau_loc, [&](int i) {
+        return double(residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs));
       });
     } else {
       status |= SV_ROW_RESIDUAL_ZERO;
@@ -451,7 +470,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_sweep(ChainParams p, int64_t t
 
 template <typename T, int VW>
 __global__ __launch_bounds__(kBlock) void k_chain_decide(ChainParams p) {
-  __shared__ FinishShared sh;
+  __shared__ DecideShared sh;
   decide_sequence<T, VW>(p, blockIdx.x, sh);
 }
 
@@ -473,17 +492,20 @@ __global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p
   const float kk = log2e_over_t(te);
   const RowPart pt = p.part[(b * R + jt) * p.nchunk + c];
   const RowPart pd = p.part[(b * R + jd) * p.nchunk + c];
-  const double A = chunk_scale(pt.m, p.rowstat[b * R + jt], Td);
-  const double Bq = chunk_scale(pd.m, p.rowstat[b * R + jd], Td);
-  float zt[kElemsPerLane], zd[kElemsPerLane];
-  load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jt, p.V), p.V, c, lane, zt);
-  load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jd, p.V), p.V, c, lane, zd);
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  const ResidualScale rs = residual_scale(chunk_scale(pt.m, p.rowstat[b * R + jt], Td),
+                                          chunk_scale(pd.m, p.rowstat[b * R + jd], Td));
+  double wsum = 0.0;
+  if (rs.A > 0.0) {  // wave-uniform
+    float zt[kElemsPerLane], zd[kElemsPerLane];
+    load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jt, p.V), p.V, c, lane, zt);
+    load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jd, p.V), p.V, c, lane, zd);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int i = 0; i < kElemsPerLane; ++i)
-    acc[i & 3] += residual_term(zt[i], zd[i], pt.m, pd.m, kk, A, Bq);
-  const double s = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
-  if (lane == 0) p.wres[w] = s;
+    for (int i = 0; i < kElemsPerLane; ++i)
+      acc[i & 3] += double(residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs));
+    wsum = rs.A * wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  }
+  if (lane == 0) p.wres[w] = wsum;
 }
 
 template <typename T, int VW>

@@ -57,21 +57,13 @@ struct __attribute__((aligned(16))) ArgPart {
   int32_t pad;
 };
 
-// Workgroups of the sweep kernels: 16 waves, one chunk each, all chunks of one sequence (or
-// tree) contiguous in blockIdx.
-constexpr int kChunksPerGroup = 16;
-
-// Completion counters sit 256 bytes apart: counters sharing a line serialise the device-scope
-// atomics of concurrently finishing sequences (measured: +37% sweep time when packed).
-constexpr int kCounterStride = 64;
+// Grid sizing for the 32-bit launch limit: workgroups of four waves, one (row, chunk) pair
+// per wave.
+constexpr int kChunksPerGroup = 4;
 
 inline int64_t groups_per_unit(int64_t rows_per_unit, int64_t V) {
   return (rows_per_unit * n_chunks(V) + kChunksPerGroup - 1) / kChunksPerGroup;
 }
-
-// Workgroups are dealt round-robin to the XCDs; this many XCDs are assumed when laying out
-// logical work per XCD (any value keeps the mapping a bijection; 8 matches MI355X).
-constexpr int kXcds = 8;
 
 // Workspace: per (row, chunk) partials, per row statistics, per sequence decisions, per
 // (sequence, chunk) residual masses.  Every entry is written before it is read within a call.
@@ -97,21 +89,17 @@ inline ChainLayout chain_layout(int64_t B, int64_t gamma, int64_t V) {
   return L;
 }
 
-// Workspace: per (row, chunk) argmax partials, one completion counter per tree.
+// Workspace: per (row, chunk) argmax partials.
 struct TreeLayout {
   int64_t nchunk;
-  size_t off_part, off_counter, total;
+  size_t off_part, total;
 };
 
 inline TreeLayout tree_layout(int64_t n_trees, int64_t n_nodes, int64_t V) {
   TreeLayout L;
   L.nchunk = n_chunks(V);
-  size_t off = 0;
-  L.off_part = off;
-  off += align256(sizeof(ArgPart) * size_t(n_trees) * size_t(n_nodes) * size_t(L.nchunk));
-  L.off_counter = off;
-  off += align256(sizeof(int32_t) * kCounterStride * size_t(n_trees));
-  L.total = off;
+  L.off_part = 0;
+  L.total = align256(sizeof(ArgPart) * size_t(n_trees) * size_t(n_nodes) * size_t(L.nchunk));
   return L;
 }
 

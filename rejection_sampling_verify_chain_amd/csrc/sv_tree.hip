@@ -7,15 +7,14 @@
 // that output and appends the agreeing run.  Greedy outputs are per-node argmaxes.
 //
 // Two launches per call:
-//   init    zeroes one completion counter per tree.
-//   verify  the single HBM sweep: workgroups are laid out tree by tree, each of the 16 waves
-//           of a workgroup owns one chunk (2048 elements) of one node's logit row and writes
-//           the chunk maximum over non-NaN entries and the lowest index attaining it.  The
-//           last workgroup of a tree to finish merges the partials into g[u] for every
-//           node, validates the parent array, and walks from the root with one wave: at
-//           node u a ballot over the nodes finds the lowest-id child c with parent u and
-//           token g[u]; it writes the accepted path and tokens, then g of the last accepted
-//           node as the bonus token.
+//   argmax  the single HBM sweep: each wave owns one chunk (2048 elements) of one node's logit
+//           row and writes the chunk maximum over non-NaN entries and the lowest index
+//           attaining it.
+//   walk    one workgroup per tree merges the partials into g[u] for every node (one wave per
+//           node, all partial loads in flight together), validates the parent array, and walks
+//           from the root with one wave: at node u a ballot over the nodes finds the lowest-id
+//           child c with parent u and token g[u]; it writes the accepted path and tokens, then
+//           g of the last accepted node as the bonus token.
 
 #include <math.h>
 
@@ -26,20 +25,18 @@
 namespace sv {
 namespace {
 
-constexpr int kBlock = 1024;
+constexpr int kBlock = 256;  // argmax sweep: one chunk per wave
 constexpr int kWavesPerBlock = kBlock / kWave;
-static_assert(kWavesPerBlock == kChunksPerGroup, "one chunk per wave");
+constexpr int kWalkBlock = 1024;  // walk: one wave per node during the merge
 
 struct TreeParams {
   const void* logits;
   const int32_t* parents;
   const int32_t* node_tokens;
   int n_nodes;
-  int wg_per_tree;
   int64_t V;
   int64_t nchunk;
   ArgPart* part;
-  int32_t* counter;
   int32_t* out_path;
   int32_t* out_tokens;
   int32_t* out_nacc;
@@ -104,7 +101,7 @@ __device__ void merge_node(const ArgPart* pp, int64_t nchunk, int lane, int32_t*
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       const int64_t c = base + i * kWave + lane;
-      r[i] = c < nchunk ? fetch(&pp[c]) : ArgPart{-INFINITY, INT32_MAX, 0, 0};
+      r[i] = c < nchunk ? pp[c] : ArgPart{-INFINITY, INT32_MAX, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
@@ -128,7 +125,7 @@ __device__ void merge_node(const ArgPart* pp, int64_t nchunk, int lane, int32_t*
   *nan = __any(anynan);
 }
 
-// Completes tree t once every chunk partial of it is in `part` (all threads of the group).
+// Completes tree t from its chunk partials (all threads of the workgroup).
 __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
   const int n_nodes = p.n_nodes;
   const int64_t base = t * n_nodes;
@@ -138,7 +135,7 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
   if (threadIdx.x == 0) sh.flags = 0;
   __syncthreads();
   int local = 0;
-  for (int u = wave; u < n_nodes; u += kWavesPerBlock) {
+  for (int u = wave; u < n_nodes; u += kWalkBlock / kWave) {
     int32_t gu;
     int nan;
     merge_node(p.part + (base + u) * nchunk, nchunk, lane, &gu, &nan);
@@ -148,7 +145,7 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
       if (nan) local |= SV_ROW_NONFINITE;
     }
   }
-  for (int u = threadIdx.x; u < n_nodes; u += kBlock) {
+  for (int u = threadIdx.x; u < n_nodes; u += kWalkBlock) {
     const int32_t pu = p.parents[base + u];
     const int32_t tu = p.node_tokens[base + u];
     sh.par[u] = pu;
@@ -197,41 +194,26 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_tree_init(int32_t* __restrict__ counter, int64_t n) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) counter[i * kCounterStride] = 0;
+template <typename T, int VW>
+__global__ __launch_bounds__(kBlock) void k_tree_argmax(TreeParams p, int64_t total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
+  if (w >= total) return;  // wave-uniform
+  const int64_t row = w / p.nchunk;
+  const int64_t c = w - row * p.nchunk;
+  const ArgPart a = argmax_chunk<T, VW>(static_cast<const T*>(p.logits) + row * p.V, p.V, c, lane);
+  if (lane == 0) p.part[w] = a;
 }
 
-template <typename T, int VW>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8))) void k_tree_verify(TreeParams p) {
+__global__ __launch_bounds__(kWalkBlock) void k_tree_walk(TreeParams p) {
   extern __shared__ int32_t walk_lds[];
   __shared__ WalkShared sh;
-  __shared__ int32_t is_last;
-  const int64_t lg = xcd_logical_index(blockIdx.x, gridDim.x);  // one tree range per XCD
-  const int64_t t = lg / p.wg_per_tree;
-  const int64_t g = lg - t * p.wg_per_tree;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t idx = g * kWavesPerBlock + wave;  // chunk index within the tree
-  if (idx < p.n_nodes * p.nchunk) {               // wave-uniform
-    const int64_t u = idx / p.nchunk;
-    const int64_t c = idx - u * p.nchunk;
-    const T* row = static_cast<const T*>(p.logits) + (t * p.n_nodes + u) * p.V;
-    const ArgPart a = argmax_chunk<T, VW>(row, p.V, c, lane);
-    if (lane == 0) publish(&p.part[(t * p.n_nodes + u) * p.nchunk + c], a);
-  }
-  // Partials are complete before the workgroup is counted; the last one finishes the tree.
-  wait_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = count_dev(&p.counter[t * kCounterStride]) == p.wg_per_tree - 1;
-  __syncthreads();
-  if (!is_last) return;
   if (threadIdx.x == 0) {
     sh.g = walk_lds;
     sh.par = walk_lds + p.n_nodes;
     sh.tok = walk_lds + 2 * p.n_nodes;
   }
-  finish_tree(p, t, sh);
+  finish_tree(p, blockIdx.x, sh);
 }
 
 template <typename T, int VW>
@@ -242,21 +224,20 @@ hipError_t run_tree(const TreeArgs& a, hipStream_t s) {
   p.parents = a.parents;
   p.node_tokens = a.node_tokens;
   p.n_nodes = a.n_nodes;
-  p.wg_per_tree = int(groups_per_unit(a.n_nodes, a.V));
   p.V = a.V;
   p.nchunk = L.nchunk;
   p.part = reinterpret_cast<ArgPart*>(a.ws + L.off_part);
-  p.counter = reinterpret_cast<int32_t*>(a.ws + L.off_counter);
   p.out_path = a.out_path;
   p.out_tokens = a.out_tokens;
   p.out_nacc = a.out_num_accepted;
   p.out_g = a.out_node_argmax;
   p.out_status = a.out_status;
-  hipError_t e = launch_kernel("tree_init", k_tree_init, dim3(unsigned((a.n_trees + 255) / 256)),
-                               dim3(256), s, p.counter, int64_t(a.n_trees));
+  const int64_t total = int64_t(a.n_trees) * a.n_nodes * L.nchunk;
+  hipError_t e = launch_kernel("tree_argmax", k_tree_argmax<T, VW>,
+                               dim3(unsigned((total + kWavesPerBlock - 1) / kWavesPerBlock)),
+                               dim3(kBlock), s, p, total);
   if (e != hipSuccess) return e;
-  return launch_kernel_shm("tree_verify", k_tree_verify<T, VW>,
-                           dim3(unsigned(int64_t(a.n_trees) * p.wg_per_tree)), dim3(kBlock),
+  return launch_kernel_shm("tree_walk", k_tree_walk, dim3(unsigned(a.n_trees)), dim3(kWalkBlock),
                            size_t(3) * sizeof(int32_t) * size_t(a.n_nodes), s, p);
 }
 
