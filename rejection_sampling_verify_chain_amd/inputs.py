@@ -224,23 +224,23 @@ def chain_gaussian(seed, B, gamma, V, dtype, sigma_t, sigma_d, temperature, draf
                          s_tok, s_u, meta)
 
 
-def chain_c1(seed=1):
+def chain_b1_v1000(seed=1):
     """B=1, gamma=4, V=1000, fp32, T=1.0; z_t ~ N(0, 2^2); z_d = z_t + N(0, 0.5^2)."""
-    return chain_gaussian(seed, 1, 4, 1000, "f32", 2.0, 0.5, 1.0, name="c1")
+    return chain_gaussian(seed, 1, 4, 1000, "f32", 2.0, 0.5, 1.0, name="gauss_b1_g4_v1000_f32")
 
 
-def chain_c2(seed=2, gamma=4):
+def chain_b1_v32000(seed=2, gamma=4):
     """B=1, gamma in {4..7}, V=32000, bf16, T=0.8; z_t ~ N(0, 3^2); z_d = z_t + N(0, 1^2)."""
-    return chain_gaussian(seed, 1, gamma, 32000, "bf16", 3.0, 1.0, 0.8, name=f"c2_g{gamma}")
+    return chain_gaussian(seed, 1, gamma, 32000, "bf16", 3.0, 1.0, 0.8, name=f"gauss_b1_g{gamma}_v32000_bf16")
 
 
-def chain_c4(seed=4):
+def chain_b256_v152064(seed=4):
     """B=256, gamma=7, V=152064, fp32, T in {0.6, 1.0} per sequence;
     z_t ~ N(0, 2.5^2); z_d = 0.8 z_t + N(0, 1.5^2)."""
     s_main, s_temp = _streams(seed, 2)
     temp = np.where(np.random.default_rng(s_temp).random(256) < 0.5, 0.6, 1.0).astype(np.float32)
     return chain_gaussian(s_main, 256, 7, 152064, "f32", 2.5, 1.5, temp, draft_scale=0.8,
-                          name="c4")
+                          name="gauss_b256_g7_v152064_f32")
 
 
 def chain_zipf(seed, B, gamma, V, dtype, sigma_d, temperature=1.0, name=None):
@@ -272,9 +272,9 @@ def chain_zipf(seed, B, gamma, V, dtype, sigma_d, temperature=1.0, name=None):
                          s_tok, s_u, meta)
 
 
-def chain_c3(seed=3, sigma_d=ZIPF_DRAFT_SIGMA):
+def chain_zipf_b64_v128256(seed=3, sigma_d=ZIPF_DRAFT_SIGMA):
     """B=64, gamma=4, V=128256, bf16, T=1.0, Zipf-shaped logits, mean alpha about 0.7."""
-    return chain_zipf(seed, 64, 4, 128256, "bf16", sigma_d, 1.0, name="c3")
+    return chain_zipf(seed, 64, 4, 128256, "bf16", sigma_d, 1.0, name="zipf_b64_g4_v128256_bf16")
 
 
 def chain_from_logits(seed, target32, draft32, temperature, dtype="f32", name="custom"):
@@ -349,21 +349,21 @@ def tree_random(seed, n_trees, n_nodes, V, dtype, sigma=2.0, boost=4.0, boost_pr
                      parents, tokens, meta)
 
 
-def tree_c5(seed=5):
+def tree_16x64_v32000(seed=5):
     """16 trees x 64 nodes, depth <= 8, branching 1..4, V=32000, bf16, N(0, 2^2) logits with
     the +4 boost applied with probability 0.6."""
-    return tree_random(seed, 16, 64, 32000, "bf16", name="c5")
+    return tree_random(seed, 16, 64, 32000, "bf16", name="tree_16x64_v32000_bf16")
 
 
 # ----------------------------------------------------------------------------- registry
 
 CHAIN_WORKLOADS = {
-    "c1": chain_c1,
-    "c2_g4": lambda: chain_c2(gamma=4),
-    "c2_g5": lambda: chain_c2(gamma=5),
-    "c2_g6": lambda: chain_c2(gamma=6),
-    "c2_g7": lambda: chain_c2(gamma=7),
-    "c3": chain_c3,
-    "c4": chain_c4,
+    "gauss_b1_g4_v1000_f32": chain_b1_v1000,
+    "gauss_b1_g4_v32000_bf16": lambda: chain_b1_v32000(gamma=4),
+    "gauss_b1_g5_v32000_bf16": lambda: chain_b1_v32000(gamma=5),
+    "gauss_b1_g6_v32000_bf16": lambda: chain_b1_v32000(gamma=6),
+    "gauss_b1_g7_v32000_bf16": lambda: chain_b1_v32000(gamma=7),
+    "zipf_b64_g4_v128256_bf16": chain_zipf_b64_v128256,
+    "gauss_b256_g7_v152064_f32": chain_b256_v152064,
 }
-TREE_WORKLOADS = {"c5": tree_c5}
+TREE_WORKLOADS = {"tree_16x64_v32000_bf16": tree_16x64_v32000}

@@ -38,32 +38,32 @@ def report(name, counts):
     print(f"[parity] {name}: {counts}", flush=True)
 
 
-def test_c1():
-    b = I.chain_c1()
-    report("c1", check_chain(b, run_chain(b)))
+def test_gauss_b1_g4_v1000_f32():
+    b = I.chain_b1_v1000()
+    report(b.name, check_chain(b, run_chain(b)))
 
 
 @pytest.mark.parametrize("gamma", [4, 5, 6, 7])
-def test_c2(gamma):
-    b = I.chain_c2(gamma=gamma)
-    report(f"c2 gamma={gamma}", check_chain(b, run_chain(b)))
+def test_gauss_b1_v32000_bf16(gamma):
+    b = I.chain_b1_v32000(gamma=gamma)
+    report(b.name, check_chain(b, run_chain(b)))
 
 
-def test_c3_full():
-    b = I.chain_c3()
+def test_zipf_b64_g4_v128256_full():
+    b = I.chain_zipf_b64_v128256()
     counts = check_chain(b, run_chain(b))
-    report("c3", counts)
+    report(b.name, counts)
     assert counts["exact"] >= 48  # bands are rare; the bulk must match exactly
 
 
-def test_c4_full_size_sampled():
+def test_gauss_b256_g7_v152064_sampled():
     # Full workload, launched exactly as the benchmark launches it; the oracle checks a sample
     # of sequences covering both temperatures.
-    b = I.chain_c4()
+    b = I.chain_b256_v152064()
     out = run_chain(b)
     seqs = list(range(0, 256, 8)) + [1, 2, 3, 255]
     counts = check_chain(b, out, seqs)
-    report("c4 sampled", counts)
+    report(b.name + " sampled", counts)
     k = out["num_accepted"]
     assert np.all((k >= 0) & (k <= 7))
     assert np.all((out["tokens"][np.arange(256), k] >= 0) & (out["tokens"][np.arange(256), k] < 152064))
@@ -138,7 +138,7 @@ def test_golden_sequence_diagram():
 
 
 def test_deterministic():
-    b = I.chain_c2(gamma=7)
+    b = I.chain_b1_v32000(gamma=7)
     o1, o2 = run_chain(b), run_chain(b)
     for k in o1:
         assert np.array_equal(o1[k], o2[k]), k

@@ -28,14 +28,14 @@ def run_tree(batch, offset=0):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def test_c5():
-    b = I.tree_c5()
+def test_tree_16x64_v32000():
+    b = I.tree_16x64_v32000()
     ks = check_tree(b, run_tree(b))
-    print(f"[parity] c5 accepted per tree: {ks}", flush=True)
+    print(f"[parity] {b.name} accepted per tree: {ks}", flush=True)
 
 
-def test_c5_shape_deep_acceptance():
-    # Same shape as c5 with a boost large enough that most walks go deep.
+def test_tree_16x64_deep_acceptance():
+    # Same shape as the 16 x 64-node workload with a boost large enough that most walks go deep.
     b = I.tree_random(15, 16, 64, 32000, "bf16", boost=20.0, boost_prob=1.0)
     ks = check_tree(b, run_tree(b))
     print(f"[parity] deep accepted per tree: {ks}", flush=True)
@@ -102,7 +102,7 @@ def test_bad_trees_and_nan():
 
 
 def test_deterministic():
-    b = I.tree_c5()
+    b = I.tree_16x64_v32000()
     o1, o2 = run_tree(b), run_tree(b)
     for k in o1:
         assert np.array_equal(o1[k], o2[k]), k

@@ -23,7 +23,7 @@ def test_bf16_rounding_matches_torch():
                           .view(torch.bfloat16).float().numpy())
 
 
-@pytest.mark.parametrize("make", [I.chain_c1, lambda: I.chain_c2(gamma=5),
+@pytest.mark.parametrize("make", [I.chain_b1_v1000, lambda: I.chain_b1_v32000(gamma=5),
                                   lambda: I.chain_zipf(9, 2, 3, 4000, "bf16", 0.75)])
 def test_chain_generators_are_deterministic(make):
     a, b = make(), make()
@@ -32,15 +32,15 @@ def test_chain_generators_are_deterministic(make):
 
 
 def test_chain_shapes_and_ranges():
-    b = I.chain_c2(gamma=6)
+    b = I.chain_b1_v32000(gamma=6)
     assert b.target.shape == (1, 7, 32000) and b.draft.shape == (1, 6, 32000)
     assert b.target.dtype == np.uint16 and b.dtype == "bf16"
     assert b.draft_tokens.dtype == np.int32 and np.all((b.draft_tokens >= 0) & (b.draft_tokens < 32000))
     u = b.uniforms.astype(np.float64)
     assert np.all((u >= 0) & (u < 1)) and np.array_equal(u * 2 ** 24, np.round(u * 2 ** 24))
     assert np.all(b.temperature == np.float32(0.8))
-    c1 = I.chain_c1()
-    assert c1.target.dtype == np.float32 and c1.rows == 9 and c1.logit_bytes == 36000
+    small = I.chain_b1_v1000()
+    assert small.target.dtype == np.float32 and small.rows == 9 and small.logit_bytes == 36000
 
 
 def test_gumbel_draft_tokens_follow_q():
@@ -78,8 +78,8 @@ def test_tree_boost_lands_on_a_child_token():
                 assert int(np.argmax(t.logits[k, u])) in set(t.node_tokens[k, kids].tolist())
 
 
-def test_tree_c5_deterministic():
-    a, b = I.tree_c5(), I.tree_c5()
+def test_tree_16x64_v32000_deterministic():
+    a, b = I.tree_16x64_v32000(), I.tree_16x64_v32000()
     assert np.array_equal(a.logits, b.logits) and np.array_equal(a.parents, b.parents)
     assert a.logits.shape == (16, 64, 32000) and a.logit_bytes == 65536000
 
