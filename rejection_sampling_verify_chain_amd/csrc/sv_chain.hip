@@ -104,12 +104,21 @@ __device__ __forceinline__ float residual_term(float zt, float zd, float mt, flo
 
 // ------------------------------------------------------------------------------------ sweep
 
-// One wave: chunk c of logit row `row` -> (chunk max, fp64 sum of exp((z - max)/T)).
-template <typename T, int VW>
-__device__ __forceinline__ RowPart sweep_chunk(const T* __restrict__ row, int64_t V, int64_t c,
-                                               int lane, float k) {
-  float z[kElemsPerLane];
-  load_chunk<T, VW>(row, V, c, lane, z);
+// Sum of exp((z - m)/T) over a lane's elements: fp32 terms added in groups of four in fp32 (two
+// roundings deep), the group sums accumulated in fp64.
+template <typename TermFn>
+__device__ __forceinline__ double lane_term_sum(TermFn term) {
+  double acc[2] = {0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < kElemsPerLane; i += 4) {
+    const float t = (term(i) + term(i + 1)) + (term(i + 2) + term(i + 3));
+    acc[(i >> 2) & 1] += double(t);
+  }
+  return acc[0] + acc[1];
+}
+
+// One wave, one loaded chunk -> (chunk max, fp64 sum of exp((z - max)/T)).
+__device__ __forceinline__ RowPart reduce_chunk(const float (&z)[kElemsPerLane], float k) {
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kElemsPerLane; ++i) m = fmaxf(m, z[i]);
@@ -122,10 +131,7 @@ __device__ __forceinline__ RowPart sweep_chunk(const T* __restrict__ row, int64_
     for (int i = 0; i < kElemsPerLane; ++i) nan |= (z[i] != z[i]);
     s = __any(nan) ? NAN : 0.0;
   } else {
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int i = 0; i < kElemsPerLane; ++i) acc[i & 3] += double(softmax_term(z[i], m, k));
-    s = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    s = wave_sum(lane_term_sum([&](int i) { return softmax_term(z[i], m, k); }));
   }
   return RowPart{m, 0, s};
 }
@@ -226,7 +232,7 @@ __device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& s
   const int gamma = p.gamma;
   const int64_t V = p.V, nchunk = p.nchunk;
   const int R = 2 * gamma + 1;
-  const int wave = threadIdx.x / kWave;
+  const int wave = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
   const float tb = p.temp[b];
   const double Td = effective_temperature(tb);
@@ -453,19 +459,36 @@ __device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision
 
 template <typename T, int VW>
 __global__ __launch_bounds__(kBlock) void k_chain_sweep(ChainParams p, int64_t total) {
+  constexpr int U = units_per_wave<T>();
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
-  if (w >= total) return;  // wave-uniform
+  const int64_t w0 = (int64_t(blockIdx.x) * kWavesPerBlock + wave_id()) * U;
+  if (w0 >= total) return;  // wave-uniform
   const int R = 2 * p.gamma + 1;
-  const int64_t row = w / p.nchunk;  // b * R + j
-  const int64_t c = w - row * p.nchunk;
-  const int64_t b = row / R;
-  const int j = int(row - b * R);
-  const float k = log2e_over_t(effective_temperature(p.temp[b]));
-  const T* rp = chain_row(static_cast<const T*>(p.tgt), static_cast<const T*>(p.drf), b, p.gamma,
-                          j, p.V);
-  const RowPart part = sweep_chunk<T, VW>(rp, p.V, c, lane, k);
-  if (lane == 0) p.part[w] = part;
+  RawChunk<T, VW> raw[U];
+  float k[U];
+  // All loads of the wave's units first, so that they are in flight together.
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t w = w0 + u;
+    if (w >= total) break;
+    const int64_t row = w / p.nchunk;  // b * R + j
+    const int64_t c = w - row * p.nchunk;
+    const int64_t b = row / R;
+    const int j = int(row - b * R);
+    k[u] = log2e_over_t(effective_temperature(p.temp[b]));
+    load_raw<T, VW>(chain_row(static_cast<const T*>(p.tgt), static_cast<const T*>(p.drf), b,
+                              p.gamma, j, p.V),
+                    p.V, c, lane, raw[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t w = w0 + u;
+    if (w >= total) break;
+    float z[kElemsPerLane];
+    unpack_chunk<T, VW>(raw[u], p.V, w - (w / p.nchunk) * p.nchunk, lane, z);
+    const RowPart part = reduce_chunk(z, k[u]);
+    if (lane == 0) p.part[w] = part;
+  }
 }
 
 template <typename T, int VW>
@@ -477,7 +500,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(ChainParams p) {
 template <typename T, int VW>
 __global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p, int64_t total) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t w = int64_t(blockIdx.x) * (kResidualBlock / kWave) + threadIdx.x / kWave;
+  const int64_t w = int64_t(blockIdx.x) * (kResidualBlock / kWave) + wave_id();
   if (w >= total) return;  // wave-uniform
   const int64_t b = w / p.nchunk;
   const int64_t c = w - b * p.nchunk;
@@ -499,11 +522,8 @@ __global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p
     float zt[kElemsPerLane], zd[kElemsPerLane];
     load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jt, p.V), p.V, c, lane, zt);
     load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jd, p.V), p.V, c, lane, zd);
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int i = 0; i < kElemsPerLane; ++i)
-      acc[i & 3] += double(residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs));
-    wsum = rs.A * wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    wsum = rs.A * wave_sum(lane_term_sum(
+                      [&](int i) { return residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs); }));
   }
   if (lane == 0) p.wres[w] = wsum;
 }
@@ -539,8 +559,9 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   p.out_status = a.out_status;
 
   const int64_t total = int64_t(a.B) * (2 * a.gamma + 1) * L.nchunk;
+  const int64_t waves = (total + units_per_wave<T>() - 1) / units_per_wave<T>();
   hipError_t e = launch_kernel("chain_sweep", k_chain_sweep<T, VW>,
-                               dim3(unsigned((total + kWavesPerBlock - 1) / kWavesPerBlock)),
+                               dim3(unsigned((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                                dim3(kBlock), s, p, total);
   if (e != hipSuccess) return e;
   e = launch_kernel("chain_decide", k_chain_decide<T, VW>, dim3(unsigned(a.B)), dim3(kBlock), s, p);

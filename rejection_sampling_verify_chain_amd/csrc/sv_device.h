@@ -71,34 +71,55 @@ __device__ __forceinline__ int chunk_offset(int j, int lane, int t) {
   return (j * kWave + lane) * VW + t;
 }
 
-// Loads j in [J0, J0 + NJ) of the lane's share of chunk c into z[0 .. NJ*VW); z[(j-J0)*VW + t]
-// holds element (j, t).
-template <typename T, int VW, int J0, int NJ>
-__device__ __forceinline__ void load_chunk_part(const T* __restrict__ row, int64_t V, int64_t c,
-                                                int lane, float (&z)[NJ * VW]) {
+// A lane's share of chunk c as loaded: the raw 16-byte vectors (VW > 1), or the widened
+// elements (VW == 1).  Widening the vector forms into floats is left to unpack_chunk, so that a
+// wave can hold several chunks in flight at 4 (fp32) or 2 (bf16) elements per register.
+template <typename T, int VW>
+struct RawChunk {
+  typename Vec<T, VW>::type v[kElemsPerLane / VW];
+};
+template <typename T>
+struct RawChunk<T, 1> {
+  float v[kElemsPerLane];
+};
+
+template <typename T, int VW>
+__device__ __forceinline__ void load_raw(const T* __restrict__ row, int64_t V, int64_t c, int lane,
+                                         RawChunk<T, VW>& r) {
   const int64_t c0 = c * kChunk;
   if constexpr (VW == 1) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t e = c0 + (J0 + j) * kWave + lane;
-      z[j] = e < V ? widen(__builtin_nontemporal_load(&row[e])) : -INFINITY;
+    for (int j = 0; j < kElemsPerLane; ++j) {
+      const int64_t e = c0 + j * kWave + lane;
+      r.v[j] = e < V ? widen(__builtin_nontemporal_load(&row[e])) : -INFINITY;
     }
   } else {
     using VT = typename Vec<T, VW>::type;
     const VT* vrow = reinterpret_cast<const VT*>(row);
     const int64_t nvec = V / VW;
     const int64_t v0 = c0 / VW;
-    VT buf[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t vi = v0 + (J0 + j) * kWave + lane;
-      if (vi < nvec) buf[j] = __builtin_nontemporal_load(&vrow[vi]);
+    for (int j = 0; j < kElemsPerLane / VW; ++j) {
+      const int64_t vi = v0 + j * kWave + lane;
+      if (vi < nvec) r.v[j] = __builtin_nontemporal_load(&vrow[vi]);
     }
+  }
+}
+
+// z[j * VW + t] = element (j, t) of the lane's share, -inf beyond V.
+template <typename T, int VW>
+__device__ __forceinline__ void unpack_chunk(const RawChunk<T, VW>& r, int64_t V, int64_t c,
+                                             int lane, float (&z)[kElemsPerLane]) {
+  if constexpr (VW == 1) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t vi = v0 + (J0 + j) * kWave + lane;
-      if (vi < nvec) {
-        unpack<T, VW>(buf[j], &z[j * VW]);
+    for (int j = 0; j < kElemsPerLane; ++j) z[j] = r.v[j];
+  } else {
+    const int64_t nvec = V / VW;
+    const int64_t v0 = c * kChunk / VW;
+#pragma unroll
+    for (int j = 0; j < kElemsPerLane / VW; ++j) {
+      if (v0 + j * kWave + lane < nvec) {
+        unpack<T, VW>(r.v[j], &z[j * VW]);
       } else {
 #pragma unroll
         for (int t = 0; t < VW; ++t) z[j * VW + t] = -INFINITY;
@@ -107,10 +128,13 @@ __device__ __forceinline__ void load_chunk_part(const T* __restrict__ row, int64
   }
 }
 
+// The lane's share of chunk c, widened: z[j * VW + t] holds element (j, t).
 template <typename T, int VW>
 __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t V, int64_t c, int lane,
                                            float (&z)[kElemsPerLane]) {
-  load_chunk_part<T, VW, 0, kElemsPerLane / VW>(row, V, c, lane, z);
+  RawChunk<T, VW> r;
+  load_raw<T, VW>(row, V, c, lane, r);
+  unpack_chunk<T, VW>(r, V, c, lane, z);
 }
 
 // ---------------------------------------------------------------------------- wave collectives
@@ -151,6 +175,20 @@ __device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
 }
 
 __device__ __forceinline__ double wave_broadcast(double v, int src) { return __shfl(v, src, kWave); }
+
+// (row, chunk) units one wave of a streaming kernel takes: its loads for all of them are issued
+// together, 8 KiB per wave (one fp32 chunk, two bf16 chunks), which keeps enough bytes in
+// flight per compute unit for HBM to stay saturated while other waves compute.
+template <typename T>
+constexpr int units_per_wave() {
+  return 4 / int(sizeof(T));
+}
+
+// Index of the calling wave within its workgroup, as a wave-uniform (scalar) value: index
+// arithmetic derived from it runs on the scalar unit instead of every lane.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+}
 
 // 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

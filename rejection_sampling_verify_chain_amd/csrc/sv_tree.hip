@@ -44,12 +44,11 @@ struct TreeParams {
   int32_t* out_status;
 };
 
-// One wave: chunk c of a logit row -> (max over non-NaN entries, lowest index holding it).
-template <typename T, int VW>
-__device__ __forceinline__ ArgPart argmax_chunk(const T* __restrict__ row, int64_t V, int64_t c,
-                                                int lane) {
-  float z[kElemsPerLane];
-  load_chunk<T, VW>(row, V, c, lane, z);
+// One wave, loaded chunk c of a logit row -> (max over non-NaN entries, lowest index holding
+// it, whether the chunk holds a NaN).
+template <int VW>
+__device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane], int64_t V,
+                                                int64_t c, int lane) {
   float m = -INFINITY;
   bool nan = false;
 #pragma unroll
@@ -74,7 +73,7 @@ __device__ __forceinline__ ArgPart argmax_chunk(const T* __restrict__ row, int64
 }
 
 // Walk state in LDS, sized by the launch to 3 * n_nodes words: argmax, parent and token of
-// every node.  Only the finishing workgroup of a tree touches it.
+// every node.  Only the walk workgroup of a tree uses it.
 struct WalkShared {
   int32_t* g;
   int32_t* par;
@@ -130,7 +129,7 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
   const int n_nodes = p.n_nodes;
   const int64_t base = t * n_nodes;
   const int64_t nchunk = p.nchunk;
-  const int wave = threadIdx.x / kWave;
+  const int wave = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
   if (threadIdx.x == 0) sh.flags = 0;
   __syncthreads();
@@ -196,13 +195,30 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
 
 template <typename T, int VW>
 __global__ __launch_bounds__(kBlock) void k_tree_argmax(TreeParams p, int64_t total) {
+  constexpr int U = units_per_wave<T>();
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
-  if (w >= total) return;  // wave-uniform
-  const int64_t row = w / p.nchunk;
-  const int64_t c = w - row * p.nchunk;
-  const ArgPart a = argmax_chunk<T, VW>(static_cast<const T*>(p.logits) + row * p.V, p.V, c, lane);
-  if (lane == 0) p.part[w] = a;
+  const int64_t w0 = (int64_t(blockIdx.x) * kWavesPerBlock + wave_id()) * U;
+  if (w0 >= total) return;  // wave-uniform
+  RawChunk<T, VW> raw[U];
+  // All loads of the wave's units first, so that they are in flight together.
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t w = w0 + u;
+    if (w >= total) break;
+    const int64_t row = w / p.nchunk;
+    load_raw<T, VW>(static_cast<const T*>(p.logits) + row * p.V, p.V, w - row * p.nchunk, lane,
+                    raw[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t w = w0 + u;
+    if (w >= total) break;
+    const int64_t c = w - (w / p.nchunk) * p.nchunk;
+    float z[kElemsPerLane];
+    unpack_chunk<T, VW>(raw[u], p.V, c, lane, z);
+    const ArgPart a = argmax_chunk<VW>(z, p.V, c, lane);
+    if (lane == 0) p.part[w] = a;
+  }
 }
 
 __global__ __launch_bounds__(kWalkBlock) void k_tree_walk(TreeParams p) {
@@ -233,8 +249,9 @@ hipError_t run_tree(const TreeArgs& a, hipStream_t s) {
   p.out_g = a.out_node_argmax;
   p.out_status = a.out_status;
   const int64_t total = int64_t(a.n_trees) * a.n_nodes * L.nchunk;
+  const int64_t waves = (total + units_per_wave<T>() - 1) / units_per_wave<T>();
   hipError_t e = launch_kernel("tree_argmax", k_tree_argmax<T, VW>,
-                               dim3(unsigned((total + kWavesPerBlock - 1) / kWavesPerBlock)),
+                               dim3(unsigned((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                                dim3(kBlock), s, p, total);
   if (e != hipSuccess) return e;
   return launch_kernel_shm("tree_walk", k_tree_walk, dim3(unsigned(a.n_trees)), dim3(kWalkBlock),
