@@ -49,27 +49,54 @@ struct TreeParams {
 template <int VW>
 __device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane], int64_t V,
                                                 int64_t c, int lane) {
+  constexpr int NJ = kElemsPerLane / VW;
   float m = -INFINITY;
-  bool nan = false;
+  uint64_t nan = 0;
 #pragma unroll
   for (int i = 0; i < kElemsPerLane; ++i) {
     m = fmaxf(m, z[i]);  // NaN never wins
-    nan |= (z[i] != z[i]);
+    nan |= __ballot(z[i] != z[i]);
   }
   m = wave_max(m);
-  // Lowest element index holding m: within a lane, (j, t) order is increasing index.
   int idx = INT32_MAX;
+  if (m > -INFINITY) {
+    // Lowest chunk offset holding m, from one lane mask per element taken on the scalar unit:
+    // offsets increase with j, then lane, then t.  Elements beyond V hold -inf and cannot
+    // match a finite or +inf maximum, so no bounds test is needed here.
+    bool found = false;
 #pragma unroll
-  for (int j = kElemsPerLane / VW - 1; j >= 0; --j) {
+    for (int j = 0; j < NJ; ++j) {
+      uint64_t mt[VW];
+      uint64_t any = 0;
 #pragma unroll
-    for (int t = VW - 1; t >= 0; --t) {
-      const int off = chunk_offset<VW>(j, lane, t);
-      if (z[j * VW + t] == m && c * kChunk + off < V) idx = off;
+      for (int t = 0; t < VW; ++t) {
+        mt[t] = __ballot(z[j * VW + t] == m);
+        any |= mt[t];
+      }
+      if (!found && any != 0) {
+        const int l = __builtin_ctzll(any);
+        int tt = 0;
+#pragma unroll
+        for (int t = VW - 1; t >= 0; --t)
+          if ((mt[t] >> l) & 1) tt = t;
+        idx = chunk_offset<VW>(j, l, tt);
+        found = true;
+      }
     }
+  } else {
+    // No finite value: the lowest in-range -inf element, if any (padding is -inf too).
+    int li = INT32_MAX;
+#pragma unroll
+    for (int j = NJ - 1; j >= 0; --j) {
+#pragma unroll
+      for (int t = VW - 1; t >= 0; --t) {
+        const int off = chunk_offset<VW>(j, lane, t);
+        if (z[j * VW + t] == m && c * kChunk + off < V) li = off;
+      }
+    }
+    idx = wave_min(li);
   }
-  idx = wave_min(idx);
-  const int any_nan = __any(nan);
-  return ArgPart{m, idx == INT32_MAX ? INT32_MAX : int32_t(c * kChunk + idx), any_nan, 0};
+  return ArgPart{m, idx == INT32_MAX ? INT32_MAX : int32_t(c * kChunk + idx), nan != 0, 0};
 }
 
 // Walk state in LDS, sized by the launch to 3 * n_nodes words: argmax, parent and token of
