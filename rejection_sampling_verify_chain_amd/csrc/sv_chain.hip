@@ -35,7 +35,7 @@
 namespace sv {
 namespace {
 
-constexpr int kBlock = 1024;  // sweep and decide
+constexpr int kBlock = 1024;  // decide: one wave per row of a sequence
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kResidualBlock = 256;  // residual: one chunk per wave
 
@@ -117,22 +117,16 @@ __device__ __forceinline__ double lane_term_sum(TermFn term) {
   return acc[0] + acc[1];
 }
 
-// One wave, one loaded chunk -> (chunk max, fp64 sum of exp((z - max)/T)).
+// One wave, one loaded chunk -> (chunk max, fp64 sum of exp((z - max)/T)).  Branch-free: a
+// chunk with no value above -inf takes 0 as the exponent's reference, so its -inf terms are
+// exp(-inf) = 0 and a NaN still poisons the sum (as does a +inf maximum, through inf - inf).
 __device__ __forceinline__ RowPart reduce_chunk(const float (&z)[kElemsPerLane], float k) {
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kElemsPerLane; ++i) m = fmaxf(m, z[i]);
   m = wave_max(m);
-  double s;
-  if (m == -INFINITY) {
-    // Only -inf (or NaN) in this chunk: its mass is zero unless a NaN poisons the row.
-    bool nan = false;
-#pragma unroll
-    for (int i = 0; i < kElemsPerLane; ++i) nan |= (z[i] != z[i]);
-    s = __any(nan) ? NAN : 0.0;
-  } else {
-    s = wave_sum(lane_term_sum([&](int i) { return softmax_term(z[i], m, k); }));
-  }
+  const float ref = m == -INFINITY ? 0.0f : m;
+  const double s = wave_sum(lane_term_sum([&](int i) { return softmax_term(z[i], ref, k); }));
   return RowPart{m, 0, s};
 }
 
@@ -458,37 +452,25 @@ __device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision
 // ------------------------------------------------------------------------------------ kernels
 
 template <typename T, int VW>
-__global__ __launch_bounds__(kBlock) void k_chain_sweep(ChainParams p, int64_t total) {
-  constexpr int U = units_per_wave<T>();
+__global__ __launch_bounds__(kStreamBlock<T>, kStreamWavesPerSimd<VW>) void k_chain_sweep(
+    ChainParams p, int64_t total) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t w0 = (int64_t(blockIdx.x) * kWavesPerBlock + wave_id()) * U;
-  if (w0 >= total) return;  // wave-uniform
-  const int R = 2 * p.gamma + 1;
-  RawChunk<T, VW> raw[U];
-  float k[U];
-  // All loads of the wave's units first, so that they are in flight together.
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t w = w0 + u;
-    if (w >= total) break;
-    const int64_t row = w / p.nchunk;  // b * R + j
-    const int64_t c = w - row * p.nchunk;
-    const int64_t b = row / R;
-    const int j = int(row - b * R);
-    k[u] = log2e_over_t(effective_temperature(p.temp[b]));
-    load_raw<T, VW>(chain_row(static_cast<const T*>(p.tgt), static_cast<const T*>(p.drf), b,
-                              p.gamma, j, p.V),
-                    p.V, c, lane, raw[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t w = w0 + u;
-    if (w >= total) break;
-    float z[kElemsPerLane];
-    unpack_chunk<T, VW>(raw[u], p.V, w - (w / p.nchunk) * p.nchunk, lane, z);
-    const RowPart part = reduce_chunk(z, k[u]);
-    if (lane == 0) p.part[w] = part;
-  }
+  const int64_t gw = int64_t(blockIdx.x) * (kStreamBlock<T> / kWave) + wave_id();
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  stream_wave<RawChunk<T, VW>, kUnitsPerWave<T>>(
+      gw, total, p.nchunk, 2 * p.gamma + 1,
+      [&](const Unit& k, RawChunk<T, VW>& r) {
+        load_raw<T, VW>(chain_row(tgt, drf, k.b, p.gamma, k.j, p.V) + int64_t(k.c) * kChunk,
+                        chunk_valid(p.V, k.c), lane, r);
+      },
+      [&](const Unit& k, const RawChunk<T, VW>& r) {
+        float z[kElemsPerLane];
+        unpack_chunk<T, VW>(r, chunk_valid(p.V, k.c), lane, z);
+        const RowPart rp =
+            reduce_chunk(z, log2e_over_t(effective_temperature(uniform_load(p.temp, k.b))));
+        if (lane == 0) p.part[k.w] = rp;
+      });
 }
 
 template <typename T, int VW>
@@ -559,10 +541,11 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   p.out_status = a.out_status;
 
   const int64_t total = int64_t(a.B) * (2 * a.gamma + 1) * L.nchunk;
-  const int64_t waves = (total + units_per_wave<T>() - 1) / units_per_wave<T>();
+  const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
+  constexpr int wpb = kStreamBlock<T> / kWave;
   hipError_t e = launch_kernel("chain_sweep", k_chain_sweep<T, VW>,
-                               dim3(unsigned((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
-                               dim3(kBlock), s, p, total);
+                               dim3(unsigned((waves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
+                               p, total);
   if (e != hipSuccess) return e;
   e = launch_kernel("chain_decide", k_chain_decide<T, VW>, dim3(unsigned(a.B)), dim3(kBlock), s, p);
   if (e != hipSuccess) return e;

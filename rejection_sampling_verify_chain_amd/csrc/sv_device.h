@@ -17,12 +17,13 @@ __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint
 // ---------------------------------------------------------------------------- chunk loads
 //
 // A chunk is kChunk consecutive elements of one logit row.  Lane `lane` of the
-// wave that owns chunk c issues kElemsPerLane / VW loads of VW elements each;
+// wave that owns a chunk issues kElemsPerLane / VW loads of VW elements each;
 // load j covers the VW elements starting at chunk offset (j * 64 + lane) * VW,
 // so every load instruction reads 64 * VW consecutive elements (1 KiB for the
 // 16-byte vector forms).  Element (j, t) of a lane lands in z[j * VW + t]; the
-// chunk's element order is (j, lane, t) lexicographic.  Elements at or beyond V
-// are not read and are set to -inf.
+// chunk's element order is (j, lane, t) lexicographic.  Only the first `nvalid`
+// elements of a chunk exist (kChunk for every chunk but a row's last); the
+// others are not read and are set to -inf.
 //
 // VW = 4 (fp32) and VW = 8 (bf16) are 16-byte loads and require a 16-byte
 // aligned row start and V % VW == 0 (checked on the host); VW = 1 reads one
@@ -71,7 +72,13 @@ __device__ __forceinline__ int chunk_offset(int j, int lane, int t) {
   return (j * kWave + lane) * VW + t;
 }
 
-// A lane's share of chunk c as loaded: the raw 16-byte vectors (VW > 1), or the widened
+// Elements of chunk c of a row of V that lie inside the row (wave-uniform).
+__device__ __forceinline__ int chunk_valid(int64_t V, int64_t c) {
+  const int64_t r = V - c * kChunk;
+  return r >= kChunk ? kChunk : int(r);
+}
+
+// A lane's share of a chunk as loaded: the raw 16-byte vectors (VW > 1), or the widened
 // elements (VW == 1).  Widening the vector forms into floats is left to unpack_chunk, so that a
 // wave can hold several chunks in flight at 4 (fp32) or 2 (bf16) elements per register.
 template <typename T, int VW>
@@ -83,58 +90,142 @@ struct RawChunk<T, 1> {
   float v[kElemsPerLane];
 };
 
+// Issue the loads of the chunk starting at `base` (nvalid >= 1 elements in range).  Every
+// lane issues the same kElemsPerLane / VW loads whatever nvalid is: in a row's last chunk the
+// loads past the row are redirected to its last in-range vector (the same cache line, so no
+// extra HBM traffic) and unpack_chunk masks them.  A fixed load count keeps the compiler's
+// wait counting exact, so a wave can reduce one chunk while the next one's loads are in flight.
 template <typename T, int VW>
-__device__ __forceinline__ void load_raw(const T* __restrict__ row, int64_t V, int64_t c, int lane,
+__device__ __forceinline__ void load_raw(const T* __restrict__ base, int nvalid, int lane,
                                          RawChunk<T, VW>& r) {
-  const int64_t c0 = c * kChunk;
   if constexpr (VW == 1) {
 #pragma unroll
     for (int j = 0; j < kElemsPerLane; ++j) {
-      const int64_t e = c0 + j * kWave + lane;
-      r.v[j] = e < V ? widen(__builtin_nontemporal_load(&row[e])) : -INFINITY;
+      const int e = j * kWave + lane;
+      r.v[j] = widen(__builtin_nontemporal_load(&base[e < nvalid ? e : nvalid - 1]));
     }
   } else {
     using VT = typename Vec<T, VW>::type;
-    const VT* vrow = reinterpret_cast<const VT*>(row);
-    const int64_t nvec = V / VW;
-    const int64_t v0 = c0 / VW;
+    const VT* vb = reinterpret_cast<const VT*>(base);
+    if (nvalid == kChunk) {
 #pragma unroll
-    for (int j = 0; j < kElemsPerLane / VW; ++j) {
-      const int64_t vi = v0 + j * kWave + lane;
-      if (vi < nvec) r.v[j] = __builtin_nontemporal_load(&vrow[vi]);
+      for (int j = 0; j < kElemsPerLane / VW; ++j)
+        r.v[j] = __builtin_nontemporal_load(&vb[j * kWave + lane]);
+    } else {
+      const int last = nvalid / VW - 1;  // nvalid is a multiple of VW on this path
+#pragma unroll
+      for (int j = 0; j < kElemsPerLane / VW; ++j)
+        r.v[j] = __builtin_nontemporal_load(&vb[min(j * kWave + lane, last)]);
     }
   }
 }
 
-// z[j * VW + t] = element (j, t) of the lane's share, -inf beyond V.
+// z[j * VW + t] = element (j, t) of the lane's share, -inf beyond the row.
 template <typename T, int VW>
-__device__ __forceinline__ void unpack_chunk(const RawChunk<T, VW>& r, int64_t V, int64_t c,
-                                             int lane, float (&z)[kElemsPerLane]) {
+__device__ __forceinline__ void unpack_chunk(const RawChunk<T, VW>& r, int nvalid, int lane,
+                                             float (&z)[kElemsPerLane]) {
   if constexpr (VW == 1) {
 #pragma unroll
     for (int j = 0; j < kElemsPerLane; ++j) z[j] = r.v[j];
   } else {
-    const int64_t nvec = V / VW;
-    const int64_t v0 = c * kChunk / VW;
+#pragma unroll
+    for (int j = 0; j < kElemsPerLane / VW; ++j) unpack<T, VW>(r.v[j], &z[j * VW]);
+  }
+  if (nvalid != kChunk) {
 #pragma unroll
     for (int j = 0; j < kElemsPerLane / VW; ++j) {
-      if (v0 + j * kWave + lane < nvec) {
-        unpack<T, VW>(r.v[j], &z[j * VW]);
-      } else {
+      const bool in = (j * kWave + lane) * VW < nvalid;
 #pragma unroll
-        for (int t = 0; t < VW; ++t) z[j * VW + t] = -INFINITY;
-      }
+      for (int t = 0; t < VW; ++t) z[j * VW + t] = in ? z[j * VW + t] : -INFINITY;
     }
   }
 }
 
-// The lane's share of chunk c, widened: z[j * VW + t] holds element (j, t).
+// The lane's share of chunk c of a row of V elements, widened.
 template <typename T, int VW>
 __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t V, int64_t c, int lane,
                                            float (&z)[kElemsPerLane]) {
   RawChunk<T, VW> r;
-  load_raw<T, VW>(row, V, c, lane, r);
-  unpack_chunk<T, VW>(r, V, c, lane, z);
+  const int nvalid = chunk_valid(V, c);
+  load_raw<T, VW>(row + c * kChunk, nvalid, lane, r);
+  unpack_chunk<T, VW>(r, nvalid, lane, z);
+}
+
+// ---------------------------------------------------------------------------- streaming waves
+//
+// The streaming kernels (softmax partials, argmax partials) give each wave 8 KiB of logits to
+// load at once: one fp32 chunk or two consecutive bf16 chunks, both loads issued before either
+// is reduced.  Units are the chunks of all rows in row-major order, unit w = row * nchunk + c
+// (a row's last chunk may be partial), rows coming in groups of R (the rows of one sequence).
+// Measured alternatives that lost: a persistent grid-stride loop with the next unit's loads in
+// flight (slower at every size here), and moving the partial chunks into waves of their own
+// (2% slower on a 2.3 GB fp32 sweep).
+
+// Units a wave takes: 8 KiB of logits in flight per wave.
+template <typename T>
+constexpr int kUnitsPerWave = 4 / int(sizeof(T));
+
+// Workgroup size of the streaming kernels (measured): 1024 threads for fp32 logits, 256 for bf16.
+template <typename T>
+constexpr int kStreamBlock = sizeof(T) == 4 ? 1024 : 256;
+
+// Occupancy the vector-load streaming kernels are compiled for: 8 waves per SIMD (at most 64
+// VGPRs, reached without spills).  The one-element-load forms (unaligned rows) are left
+// unconstrained.
+template <int VW>
+constexpr int kStreamWavesPerSimd = VW > 1 ? 8 : 1;
+
+struct Unit {
+  int64_t w;  // unit index
+  int64_t b;  // group (row / R)
+  int32_t j;  // row within the group
+  int32_t c;  // chunk within the row
+};
+
+__device__ __forceinline__ Unit unit_at(int64_t w, int64_t nchunk, int R) {
+  const int64_t row = w / nchunk;
+  Unit k;
+  k.w = w;
+  k.c = int32_t(w - row * nchunk);
+  k.b = row / R;
+  k.j = int32_t(row - k.b * R);
+  return k;
+}
+
+__device__ __forceinline__ Unit unit_after(Unit k, int64_t nchunk, int R) {
+  k.w += 1;
+  if (++k.c == nchunk) {
+    k.c = 0;
+    if (++k.j == R) {
+      k.j = 0;
+      k.b += 1;
+    }
+  }
+  return k;
+}
+
+// Runs wave gw of a streaming kernel over `total` units: issue(unit, raw) starts a unit's loads
+// and proc(unit, raw) reduces it.  Wave-uniform control flow.
+template <typename Raw, int U, typename IssueFn, typename ProcFn>
+__device__ __forceinline__ void stream_wave(int64_t gw, int64_t total, int64_t nchunk, int R,
+                                            IssueFn issue, ProcFn proc) {
+  static_assert(U == 1 || U == 2, "one or two units per wave");
+  const int64_t w0 = gw * U;
+  if (w0 >= total) return;
+  const Unit k0 = unit_at(w0, nchunk, R);
+  Raw r0;
+  issue(k0, r0);
+  if constexpr (U == 2) {
+    if (w0 + 1 < total) {
+      const Unit k1 = unit_after(k0, nchunk, R);
+      Raw r1;
+      issue(k1, r1);
+      proc(k0, r0);
+      proc(k1, r1);
+      return;
+    }
+  }
+  proc(k0, r0);
 }
 
 // ---------------------------------------------------------------------------- wave collectives
@@ -176,18 +267,17 @@ __device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
 
 __device__ __forceinline__ double wave_broadcast(double v, int src) { return __shfl(v, src, kWave); }
 
-// (row, chunk) units one wave of a streaming kernel takes: its loads for all of them are issued
-// together, 8 KiB per wave (one fp32 chunk, two bf16 chunks), which keeps enough bytes in
-// flight per compute unit for HBM to stay saturated while other waves compute.
-template <typename T>
-constexpr int units_per_wave() {
-  return 4 / int(sizeof(T));
-}
-
 // Index of the calling wave within its workgroup, as a wave-uniform (scalar) value: index
 // arithmetic derived from it runs on the scalar unit instead of every lane.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+}
+
+// Wave-uniform read of read-only data through the scalar data cache (a scalar load, counted
+// apart from the vector loads, so waiting for it never waits for chunk loads in flight).
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
 }
 
 // 2^x on the hardware transcendental unit (v_exp_f32).

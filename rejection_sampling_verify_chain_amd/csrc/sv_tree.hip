@@ -25,8 +25,6 @@
 namespace sv {
 namespace {
 
-constexpr int kBlock = 256;  // argmax sweep: one chunk per wave
-constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kWalkBlock = 1024;  // walk: one wave per node during the merge
 
 struct TreeParams {
@@ -44,59 +42,32 @@ struct TreeParams {
   int32_t* out_status;
 };
 
-// One wave, loaded chunk c of a logit row -> (max over non-NaN entries, lowest index holding
-// it, whether the chunk holds a NaN).
-template <int VW>
-__device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane], int64_t V,
-                                                int64_t c, int lane) {
-  constexpr int NJ = kElemsPerLane / VW;
+// One wave, one loaded chunk whose first nvalid elements exist -> (max over non-NaN entries,
+// lowest chunk offset holding it (INT32_MAX if none), whether the chunk holds a NaN).  The
+// offset is relative to the chunk start.  Each lane finds its lowest slot i = j * VW + t holding
+// the maximum (slots increase with the chunk offset inside a lane), then a wave minimum over
+// the offsets gives the chunk's lowest.  Branch-free; a chunk of only -inf finds its first
+// in-range -inf element, a chunk of only NaN none.
+template <int VW, bool TAIL>
+__device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane], int nvalid,
+                                                int lane) {
   float m = -INFINITY;
-  uint64_t nan = 0;
+  bool nan = false;
 #pragma unroll
   for (int i = 0; i < kElemsPerLane; ++i) {
     m = fmaxf(m, z[i]);  // NaN never wins
-    nan |= __ballot(z[i] != z[i]);
+    nan |= (z[i] != z[i]);
   }
   m = wave_max(m);
-  int idx = INT32_MAX;
-  if (m > -INFINITY) {
-    // Lowest chunk offset holding m, from one lane mask per element taken on the scalar unit:
-    // offsets increase with j, then lane, then t.  Elements beyond V hold -inf and cannot
-    // match a finite or +inf maximum, so no bounds test is needed here.
-    bool found = false;
+  int slot = kElemsPerLane;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      uint64_t mt[VW];
-      uint64_t any = 0;
-#pragma unroll
-      for (int t = 0; t < VW; ++t) {
-        mt[t] = __ballot(z[j * VW + t] == m);
-        any |= mt[t];
-      }
-      if (!found && any != 0) {
-        const int l = __builtin_ctzll(any);
-        int tt = 0;
-#pragma unroll
-        for (int t = VW - 1; t >= 0; --t)
-          if ((mt[t] >> l) & 1) tt = t;
-        idx = chunk_offset<VW>(j, l, tt);
-        found = true;
-      }
-    }
-  } else {
-    // No finite value: the lowest in-range -inf element, if any (padding is -inf too).
-    int li = INT32_MAX;
-#pragma unroll
-    for (int j = NJ - 1; j >= 0; --j) {
-#pragma unroll
-      for (int t = VW - 1; t >= 0; --t) {
-        const int off = chunk_offset<VW>(j, lane, t);
-        if (z[j * VW + t] == m && c * kChunk + off < V) li = off;
-      }
-    }
-    idx = wave_min(li);
+  for (int i = kElemsPerLane - 1; i >= 0; --i) {
+    bool hit = z[i] == m;
+    if (TAIL) hit = hit && chunk_offset<VW>(i / VW, lane, i % VW) < nvalid;
+    slot = hit ? i : slot;
   }
-  return ArgPart{m, idx == INT32_MAX ? INT32_MAX : int32_t(c * kChunk + idx), nan != 0, 0};
+  const int off = slot < kElemsPerLane ? chunk_offset<VW>(slot / VW, lane, slot % VW) : INT32_MAX;
+  return ArgPart{m, wave_min(off), __any(nan) ? 1 : 0, 0};
 }
 
 // Walk state in LDS, sized by the launch to 3 * n_nodes words: argmax, parent and token of
@@ -221,31 +192,26 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
 }
 
 template <typename T, int VW>
-__global__ __launch_bounds__(kBlock) void k_tree_argmax(TreeParams p, int64_t total) {
-  constexpr int U = units_per_wave<T>();
+__global__ __launch_bounds__(kStreamBlock<T>, kStreamWavesPerSimd<VW>) void k_tree_argmax(
+    TreeParams p, int64_t total) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t w0 = (int64_t(blockIdx.x) * kWavesPerBlock + wave_id()) * U;
-  if (w0 >= total) return;  // wave-uniform
-  RawChunk<T, VW> raw[U];
-  // All loads of the wave's units first, so that they are in flight together.
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t w = w0 + u;
-    if (w >= total) break;
-    const int64_t row = w / p.nchunk;
-    load_raw<T, VW>(static_cast<const T*>(p.logits) + row * p.V, p.V, w - row * p.nchunk, lane,
-                    raw[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t w = w0 + u;
-    if (w >= total) break;
-    const int64_t c = w - (w / p.nchunk) * p.nchunk;
-    float z[kElemsPerLane];
-    unpack_chunk<T, VW>(raw[u], p.V, c, lane, z);
-    const ArgPart a = argmax_chunk<VW>(z, p.V, c, lane);
-    if (lane == 0) p.part[w] = a;
-  }
+  const int64_t gw = int64_t(blockIdx.x) * (kStreamBlock<T> / kWave) + wave_id();
+  const T* logits = static_cast<const T*>(p.logits);
+  stream_wave<RawChunk<T, VW>, 1>(
+      gw, total, p.nchunk, 1,
+      [&](const Unit& k, RawChunk<T, VW>& r) {
+        load_raw<T, VW>(logits + k.b * p.V + int64_t(k.c) * kChunk, chunk_valid(p.V, k.c), lane,
+                        r);
+      },
+      [&](const Unit& k, const RawChunk<T, VW>& r) {
+        const int nvalid = chunk_valid(p.V, k.c);
+        float z[kElemsPerLane];
+        unpack_chunk<T, VW>(r, nvalid, lane, z);
+        ArgPart a = nvalid == kChunk ? argmax_chunk<VW, false>(z, nvalid, lane)
+                                     : argmax_chunk<VW, true>(z, nvalid, lane);
+        a.idx = a.idx == INT32_MAX ? INT32_MAX : a.idx + k.c * kChunk;
+        if (lane == 0) p.part[k.w] = a;
+      });
 }
 
 __global__ __launch_bounds__(kWalkBlock) void k_tree_walk(TreeParams p) {
@@ -275,11 +241,13 @@ hipError_t run_tree(const TreeArgs& a, hipStream_t s) {
   p.out_nacc = a.out_num_accepted;
   p.out_g = a.out_node_argmax;
   p.out_status = a.out_status;
+  // One chunk per wave: at 64 registers the argmax runs 8 waves per SIMD, which measured
+  // faster than two bf16 chunks per wave at the lower occupancy their registers allow.
   const int64_t total = int64_t(a.n_trees) * a.n_nodes * L.nchunk;
-  const int64_t waves = (total + units_per_wave<T>() - 1) / units_per_wave<T>();
+  constexpr int wpb = kStreamBlock<T> / kWave;
   hipError_t e = launch_kernel("tree_argmax", k_tree_argmax<T, VW>,
-                               dim3(unsigned((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
-                               dim3(kBlock), s, p, total);
+                               dim3(unsigned((total + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
+                               p, total);
   if (e != hipSuccess) return e;
   return launch_kernel_shm("tree_walk", k_tree_walk, dim3(unsigned(a.n_trees)), dim3(kWalkBlock),
                            size_t(3) * sizeof(int32_t) * size_t(a.n_nodes), s, p);
