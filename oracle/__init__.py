@@ -18,6 +18,8 @@ Sources (cited by page title and section throughout):
   (候補の採用と棄却を具体例で見る).
 * SpecInfer article (abeam.tech, arXiv:2305.09781) — token-tree verification:
   basic idea (基本アイデア) and inference (推論方法).
+* The ai-compass page's worked example also defines greedy chain verification
+  (oracle/greedy.py): accept drafts while they equal the target's argmax.
 
 Pins: every function here is checked by the CPU tests against facts that do not
 come from this package (Theorem 1 by chi-square, the closed form for the
@@ -31,3 +33,4 @@ from .chain import (  # noqa: F401
     widen, softmax_fp64, verify_chain_seq, verify_chain_batch,
 )
 from .tree import argmax_first, verify_tree_one, verify_tree_batch  # noqa: F401
+from .greedy import verify_chain_greedy_seq, verify_chain_greedy_batch  # noqa: F401
