@@ -145,6 +145,41 @@ sv_status sv_verify_tree(const void* logits, sv_dtype dtype, const int32_t* pare
                          size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Greedy chain verification ("投機的デコーディングとは？LLMの回答を高速化する仕組み",
+ * ai-compass.weeybrid.co.jp, section 候補の採用と棄却を具体例で見る: candidates are kept while
+ * they equal the target's own choice; the first that differs is replaced by that choice).  The
+ * zero-temperature form of chain verification: no draft logits, no random numbers.
+ *
+ * For each sequence b: g_i = argmax_x target_logits[b, i, x] for i = 0..gamma (lowest x on
+ * ties, -0 == +0, NaN never the maximum); k = number of leading i < gamma with
+ * draft_tokens[b, i] == g_i; out_tokens[b, :] = [x_0 .. x_{k-1}, g_k, -1 ...];
+ * out_num_accepted[b] = k (k+1 tokens emitted).
+ *
+ * Arguments (device pointers, caller-owned, contiguous row-major):
+ *   target_logits  [B, gamma+1, V] of dtype; target row i scores draft token i, row gamma is
+ *                  the position after the last draft token.
+ *   draft_tokens   int32 [B, gamma].
+ *   B in [1, 2^24], gamma in [1, 64], V in [1, 2^31 - 1].
+ *   out_tokens        int32 [B, gamma+1]  (required)
+ *   out_num_accepted  int32 [B]           (required)
+ *   out_argmax        int32 [B, gamma+1]: g_i (optional, NULL)
+ *   out_status        int32 [B]: SV_ROW_* bits (optional, NULL)
+ *   workspace         at least sv_verify_chain_greedy_workspace_bytes(B, gamma, V, dtype)
+ *                     bytes, 256-byte aligned; no initialisation needed.
+ * A draft token outside [0, V) sets SV_ROW_TOKEN_RANGE and the sequence takes the fallback
+ * result k = 0, out_tokens = [g_0, -1, ...].  A NaN logit sets SV_ROW_NONFINITE; NaN entries
+ * are skipped by the argmax (a row of only NaN gives 0) and the comparison proceeds.
+ * ---------------------------------------------------------------------------------------- */
+size_t sv_verify_chain_greedy_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
+                                              sv_dtype dtype);
+
+sv_status sv_verify_chain_greedy(const void* target_logits, sv_dtype dtype,
+                                 const int32_t* draft_tokens, int32_t B, int32_t gamma, int64_t V,
+                                 int32_t* out_tokens, int32_t* out_num_accepted,
+                                 int32_t* out_argmax, int32_t* out_status, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Kernel timing (measurement support; not part of the verify step).
  *
  * sv_trace_start(capacity): from now on, each kernel the library launches (up to `capacity`

@@ -28,6 +28,7 @@ EXPORTS = (
     "sv_version", "sv_status_string",
     "sv_verify_chain_workspace_bytes", "sv_verify_chain",
     "sv_verify_tree_workspace_bytes", "sv_verify_tree",
+    "sv_verify_chain_greedy_workspace_bytes", "sv_verify_chain_greedy",
     "sv_trace_start", "sv_trace_stop", "sv_trace_kernels", "sv_trace_get",
 )
 
@@ -65,6 +66,11 @@ def load():
     lib.sv_verify_tree.restype = ctypes.c_int
     lib.sv_verify_tree.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i64,
                                    vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sv_verify_chain_greedy_workspace_bytes.restype = sz
+    lib.sv_verify_chain_greedy_workspace_bytes.argtypes = [i32, i32, i64, ctypes.c_int]
+    lib.sv_verify_chain_greedy.restype = ctypes.c_int
+    lib.sv_verify_chain_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i64,
+                                           vp, vp, vp, vp, vp, sz, vp]
     lib.sv_trace_start.restype = ctypes.c_int
     lib.sv_trace_start.argtypes = [ctypes.c_int]
     lib.sv_trace_stop.restype = ctypes.c_int
@@ -147,6 +153,10 @@ def chain_workspace_bytes(B, gamma, V, dtype):
 
 def tree_workspace_bytes(n_trees, n_nodes, V, dtype):
     return int(load().sv_verify_tree_workspace_bytes(n_trees, n_nodes, V, _DTYPE[dtype]))
+
+
+def chain_greedy_workspace_bytes(B, gamma, V, dtype):
+    return int(load().sv_verify_chain_greedy_workspace_bytes(B, gamma, V, _DTYPE[dtype]))
 
 
 def workspace(nbytes, device):
@@ -233,6 +243,41 @@ def sv_verify_tree(logits, parents, node_tokens, *, out_path=None, out_tokens=No
             "node_argmax": out_node_argmax, "status": out_status}
 
 
+def sv_verify_chain_greedy(target, draft_tokens, *, out_tokens=None, out_num_accepted=None,
+                           out_argmax=None, out_status=None, workspace_buf=None, stream=None,
+                           want_argmax=True, want_status=True):
+    """Greedy chain verification through the C ABI.
+
+    target [B, gamma+1, V] (fp32 or bf16), draft_tokens int32 [B, gamma].  Returns a dict
+    (tokens, num_accepted, argmax, status); the call is asynchronous.
+    """
+    lib = load()
+    if target.dtype not in _DTYPE:
+        raise ValueError(f"logits must be float32 or bfloat16, got {target.dtype}")
+    dev = target.device
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    _check(target, "target", None, (B, gamma + 1, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, gamma), dev)
+    out_tokens = _out(out_tokens, "out_tokens", torch.int32, (B, gamma + 1), dev)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", torch.int32, (B,), dev)
+    if want_argmax or out_argmax is not None:
+        out_argmax = _out(out_argmax, "out_argmax", torch.int32, (B, gamma + 1), dev)
+    if want_status or out_status is not None:
+        out_status = _out(out_status, "out_status", torch.int32, (B,), dev)
+    need = chain_greedy_workspace_bytes(B, gamma, V, target.dtype)
+    if workspace_buf is None:
+        workspace_buf = workspace(need, dev)
+    st = lib.sv_verify_chain_greedy(
+        _ptr(target), _DTYPE[target.dtype], _ptr(draft_tokens), B, gamma, V, _ptr(out_tokens),
+        _ptr(out_num_accepted), _ptr(out_argmax), _ptr(out_status), _ptr(workspace_buf),
+        workspace_buf.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_verify_chain_greedy")
+    return {"tokens": out_tokens, "num_accepted": out_num_accepted, "argmax": out_argmax,
+            "status": out_status}
+
+
 # ----------------------------------------------------------------------------- host arrays
 
 def chain_to_device(batch, device="cuda"):
@@ -250,6 +295,14 @@ def chain_to_device(batch, device="cuda"):
         "temperature": torch.from_numpy(batch.temperature).to(device),
         "dtype": dt,
     }
+
+
+def greedy_to_device(batch, device="cuda"):
+    """Copy a GreedyBatch to device tensors."""
+    t = torch.from_numpy(batch.target.view(np.int16) if batch.dtype == "bf16" else batch.target)
+    t = t.view(torch.bfloat16) if batch.dtype == "bf16" else t
+    return {"target": t.to(device),
+            "draft_tokens": torch.from_numpy(batch.draft_tokens).to(device)}
 
 
 def tree_to_device(batch, device="cuda"):

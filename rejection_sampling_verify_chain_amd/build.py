@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["sv_api.cpp", "sv_trace.cpp", "sv_chain.hip", "sv_tree.hip"]
+SOURCES = ["sv_api.cpp", "sv_trace.cpp", "sv_argmax.hip", "sv_chain.hip", "sv_tree.hip",
+           "sv_greedy.hip"]
 ARCH = "gfx950"
 
 

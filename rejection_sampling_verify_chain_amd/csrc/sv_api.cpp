@@ -37,6 +37,12 @@ bool tree_shape_ok(int32_t n_trees, int32_t n_nodes, int64_t V) {
   return grid_fits(n_trees, n_nodes, V);
 }
 
+bool greedy_shape_ok(int32_t B, int32_t gamma, int64_t V) {
+  if (B < 1 || B > sv::kMaxBatch || gamma < 1 || gamma > sv::kMaxGamma) return false;
+  if (V < 1 || V > int64_t(INT32_MAX)) return false;
+  return grid_fits(B, gamma + 1, V);
+}
+
 }  // namespace
 
 SV_EXPORT const char* sv_version(void) { return "specverify 0.1.0 gfx950"; }
@@ -131,4 +137,39 @@ SV_EXPORT sv_status sv_verify_tree(const void* logits, sv_dtype dtype, const int
   a.ws = static_cast<char*>(workspace);
   a.vec = aligned16(logits) && V % vec_width(dtype) == 0;
   return sv::launch_tree(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+SV_EXPORT size_t sv_verify_chain_greedy_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
+                                                        sv_dtype dtype) {
+  if (!valid_dtype(dtype) || !greedy_shape_ok(B, gamma, V)) return 0;
+  return sv::greedy_layout(B, gamma, V).total;
+}
+
+SV_EXPORT sv_status sv_verify_chain_greedy(const void* target_logits, sv_dtype dtype,
+                                           const int32_t* draft_tokens, int32_t B, int32_t gamma,
+                                           int64_t V, int32_t* out_tokens,
+                                           int32_t* out_num_accepted, int32_t* out_argmax,
+                                           int32_t* out_status, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_ERR_NULL;
+  if (!valid_dtype(dtype)) return SV_ERR_DTYPE;
+  if (!greedy_shape_ok(B, gamma, V)) return SV_ERR_SHAPE;
+  const size_t need = sv::greedy_layout(B, gamma, V).total;
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SV_ERR_WORKSPACE;
+
+  sv::GreedyArgs a;
+  a.target = target_logits;
+  a.dtype = dtype;
+  a.draft_tokens = draft_tokens;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.out_tokens = out_tokens;
+  a.out_num_accepted = out_num_accepted;
+  a.out_argmax = out_argmax;
+  a.out_status = out_status;
+  a.ws = static_cast<char*>(workspace);
+  a.vec = aligned16(target_logits) && V % vec_width(dtype) == 0;
+  return sv::launch_greedy(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

@@ -103,6 +103,20 @@ inline TreeLayout tree_layout(int64_t n_trees, int64_t n_nodes, int64_t V) {
   return L;
 }
 
+// Workspace of the greedy chain path: per (row, chunk) argmax partials of the target rows.
+struct GreedyLayout {
+  int64_t nchunk;
+  size_t off_part, total;
+};
+
+inline GreedyLayout greedy_layout(int64_t B, int64_t gamma, int64_t V) {
+  GreedyLayout L;
+  L.nchunk = n_chunks(V);
+  L.off_part = 0;
+  L.total = align256(sizeof(ArgPart) * size_t(B) * size_t(gamma + 1) * size_t(L.nchunk));
+  return L;
+}
+
 struct ChainArgs {
   const void* target;
   const void* draft;
@@ -137,8 +151,23 @@ struct TreeArgs {
   bool vec;
 };
 
+struct GreedyArgs {
+  const void* target;
+  sv_dtype dtype;
+  const int32_t* draft_tokens;
+  int32_t B, gamma;
+  int64_t V;
+  int32_t* out_tokens;
+  int32_t* out_num_accepted;
+  int32_t* out_argmax;
+  int32_t* out_status;
+  char* ws;
+  bool vec;
+};
+
 // Launch the chain kernels on `stream`; returns hipSuccess or the launch error.
 hipError_t launch_chain(const ChainArgs& a, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
+hipError_t launch_greedy(const GreedyArgs& a, hipStream_t stream);
 
 }  // namespace sv

@@ -7,9 +7,9 @@
 // that output and appends the agreeing run.  Greedy outputs are per-node argmaxes.
 //
 // Two launches per call:
-//   argmax  the single HBM sweep: each wave owns one chunk (2048 elements) of one node's logit
-//           row and writes the chunk maximum over non-NaN entries and the lowest index
-//           attaining it.
+//   argmax  the single HBM sweep (launch_argmax_rows): each wave owns one chunk (2048
+//           elements) of one node's logit row and writes the chunk maximum over non-NaN entries
+//           and the lowest index attaining it.
 //   walk    one workgroup per tree merges the partials into g[u] for every node (one wave per
 //           node, all partial loads in flight together), validates the parent array, and walks
 //           from the root with one wave: at node u a ballot over the nodes finds the lowest-id
@@ -18,6 +18,7 @@
 
 #include <math.h>
 
+#include "sv_argmax.h"
 #include "sv_device.h"
 #include "sv_internal.h"
 #include "sv_launch.h"
@@ -42,34 +43,6 @@ struct TreeParams {
   int32_t* out_status;
 };
 
-// One wave, one loaded chunk whose first nvalid elements exist -> (max over non-NaN entries,
-// lowest chunk offset holding it (INT32_MAX if none), whether the chunk holds a NaN).  The
-// offset is relative to the chunk start.  Each lane finds its lowest slot i = j * VW + t holding
-// the maximum (slots increase with the chunk offset inside a lane), then a wave minimum over
-// the offsets gives the chunk's lowest.  Branch-free; a chunk of only -inf finds its first
-// in-range -inf element, a chunk of only NaN none.
-template <int VW, bool TAIL>
-__device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane], int nvalid,
-                                                int lane) {
-  float m = -INFINITY;
-  bool nan = false;
-#pragma unroll
-  for (int i = 0; i < kElemsPerLane; ++i) {
-    m = fmaxf(m, z[i]);  // NaN never wins
-    nan |= (z[i] != z[i]);
-  }
-  m = wave_max(m);
-  int slot = kElemsPerLane;
-#pragma unroll
-  for (int i = kElemsPerLane - 1; i >= 0; --i) {
-    bool hit = z[i] == m;
-    if (TAIL) hit = hit && chunk_offset<VW>(i / VW, lane, i % VW) < nvalid;
-    slot = hit ? i : slot;
-  }
-  const int off = slot < kElemsPerLane ? chunk_offset<VW>(slot / VW, lane, slot % VW) : INT32_MAX;
-  return ArgPart{m, wave_min(off), __any(nan) ? 1 : 0, 0};
-}
-
 // Walk state in LDS, sized by the launch to 3 * n_nodes words: argmax, parent and token of
 // every node.  Only the walk workgroup of a tree uses it.
 struct WalkShared {
@@ -78,49 +51,6 @@ struct WalkShared {
   int32_t* tok;
   int32_t flags;
 };
-
-// (value, index) order of the argmax: larger value first, then lower index.
-__device__ __forceinline__ bool arg_better(float v, int32_t i, float bv, int32_t bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-// One wave merges the chunk partials of one node row: the row's argmax (lowest index among
-// equal maxima) and whether the row holds a NaN.  Lanes take chunks, all loads of a batch in
-// flight together, then a butterfly reduction with the argmax order.
-constexpr int kMergeBatch = 4;
-
-__device__ void merge_node(const ArgPart* pp, int64_t nchunk, int lane, int32_t* g, int* nan) {
-  float best = -INFINITY;
-  int32_t bidx = INT32_MAX;
-  int anynan = 0;
-  for (int64_t base = 0; base < nchunk; base += int64_t(kWave) * kMergeBatch) {
-    ArgPart r[kMergeBatch];
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
-      const int64_t c = base + i * kWave + lane;
-      r[i] = c < nchunk ? pp[c] : ArgPart{-INFINITY, INT32_MAX, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
-      if (arg_better(r[i].v, r[i].idx, best, bidx)) {
-        best = r[i].v;
-        bidx = r[i].idx;
-      }
-      anynan |= r[i].nan;
-    }
-  }
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(best, o, kWave);
-    const int32_t oi = __shfl_xor(bidx, o, kWave);
-    if (arg_better(ov, oi, best, bidx)) {
-      best = ov;
-      bidx = oi;
-    }
-  }
-  *g = bidx == INT32_MAX ? 0 : bidx;
-  *nan = __any(anynan);
-}
 
 // Completes tree t from its chunk partials (all threads of the workgroup).
 __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
@@ -135,7 +65,7 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
   for (int u = wave; u < n_nodes; u += kWalkBlock / kWave) {
     int32_t gu;
     int nan;
-    merge_node(p.part + (base + u) * nchunk, nchunk, lane, &gu, &nan);
+    merge_row_argmax(p.part + (base + u) * nchunk, nchunk, lane, &gu, &nan);
     if (lane == 0) {
       sh.g[u] = gu;
       if (p.out_g) p.out_g[base + u] = gu;
@@ -191,29 +121,6 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
   }
 }
 
-template <typename T, int VW>
-__global__ __launch_bounds__(kStreamBlock<T>, kStreamWavesPerSimd<VW>) void k_tree_argmax(
-    TreeParams p, int64_t total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t gw = int64_t(blockIdx.x) * (kStreamBlock<T> / kWave) + wave_id();
-  const T* logits = static_cast<const T*>(p.logits);
-  stream_wave<RawChunk<T, VW>, 1>(
-      gw, total, p.nchunk, 1,
-      [&](const Unit& k, RawChunk<T, VW>& r) {
-        load_raw<T, VW>(logits + k.b * p.V + int64_t(k.c) * kChunk, chunk_valid(p.V, k.c), lane,
-                        r);
-      },
-      [&](const Unit& k, const RawChunk<T, VW>& r) {
-        const int nvalid = chunk_valid(p.V, k.c);
-        float z[kElemsPerLane];
-        unpack_chunk<T, VW>(r, nvalid, lane, z);
-        ArgPart a = nvalid == kChunk ? argmax_chunk<VW, false>(z, nvalid, lane)
-                                     : argmax_chunk<VW, true>(z, nvalid, lane);
-        a.idx = a.idx == INT32_MAX ? INT32_MAX : a.idx + k.c * kChunk;
-        if (lane == 0) p.part[k.w] = a;
-      });
-}
-
 __global__ __launch_bounds__(kWalkBlock) void k_tree_walk(TreeParams p) {
   extern __shared__ int32_t walk_lds[];
   __shared__ WalkShared sh;
@@ -241,13 +148,8 @@ hipError_t run_tree(const TreeArgs& a, hipStream_t s) {
   p.out_nacc = a.out_num_accepted;
   p.out_g = a.out_node_argmax;
   p.out_status = a.out_status;
-  // One chunk per wave: at 64 registers the argmax runs 8 waves per SIMD, which measured
-  // faster than two bf16 chunks per wave at the lower occupancy their registers allow.
-  const int64_t total = int64_t(a.n_trees) * a.n_nodes * L.nchunk;
-  constexpr int wpb = kStreamBlock<T> / kWave;
-  hipError_t e = launch_kernel("tree_argmax", k_tree_argmax<T, VW>,
-                               dim3(unsigned((total + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
-                               p, total);
+  const hipError_t e = launch_argmax_rows("tree_argmax", a.logits, a.dtype, a.vec,
+                                          int64_t(a.n_trees) * a.n_nodes, a.V, p.part, s);
   if (e != hipSuccess) return e;
   return launch_kernel_shm("tree_walk", k_tree_walk, dim3(unsigned(a.n_trees)), dim3(kWalkBlock),
                            size_t(3) * sizeof(int32_t) * size_t(a.n_nodes), s, p);

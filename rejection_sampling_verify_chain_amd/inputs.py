@@ -287,6 +287,75 @@ def chain_from_logits(seed, target32, draft32, temperature, dtype="f32", name="c
                          s_tok, s_u, {"seed": seed})
 
 
+# ----------------------------------------------------------------------------- greedy chains
+
+@dataclass
+class GreedyBatch:
+    """One batch of greedy chain inputs: target logits [B, gamma+1, V] (fp32 or bf16 bit
+    patterns) and draft tokens int32 [B, gamma]; no draft logits or random numbers."""
+    name: str
+    dtype: str
+    target: np.ndarray
+    draft_tokens: np.ndarray
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.target.shape[0]
+
+    @property
+    def gamma(self):
+        return self.target.shape[1] - 1
+
+    @property
+    def V(self):
+        return self.target.shape[2]
+
+    @property
+    def rows(self):
+        return self.B * (self.gamma + 1)
+
+    @property
+    def logit_bytes(self):
+        return self.target.nbytes
+
+
+def chain_greedy_planted(seed, B, gamma, V, dtype, sigma=2.0, boost=16.0, match_prob=0.8,
+                         name=None):
+    """Greedy chain workload: target logits ~ N(0, sigma^2); in every row one token, chosen
+    uniformly, gets +boost (fp32, before rounding to the storage dtype); draft token i is row i's
+    planted token with probability match_prob, else a uniform token.  With the default boost the
+    planted token all but surely holds the row's maximum, so accepted runs are long; which token
+    actually holds the maximum is for the verify step to find."""
+    s_t, s_plant, s_tok = _streams(seed, 3)
+    t32 = np.empty((B, gamma + 1, V), dtype=np.float32)
+    tv = t32.reshape(B * (gamma + 1), V)
+
+    def fill_t(g, r0, r1):
+        tv[r0:r1] = g.standard_normal((r1 - r0, V), dtype=np.float32) * np.float32(sigma)
+
+    _fill_rows(s_t, B * (gamma + 1), max(1, (1 << 22) // max(V, 1)), fill_t)
+    gp = np.random.default_rng(s_plant)
+    plant = gp.integers(0, V, size=(B, gamma + 1))
+    tv[np.arange(B * (gamma + 1)), plant.reshape(-1)] += np.float32(boost)
+    gk = np.random.default_rng(s_tok)
+    other = gk.integers(0, V, size=(B, gamma))
+    toks = np.where(gk.random((B, gamma)) < match_prob, plant[:, :gamma], other).astype(np.int32)
+    meta = {"sigma": sigma, "boost": boost, "match_prob": match_prob, "seed": seed}
+    return GreedyBatch(name or f"greedy_B{B}_g{gamma}_V{V}_{dtype}", dtype, _store(t32, dtype),
+                       toks, meta)
+
+
+def chain_greedy_b256_v152064(seed=6):
+    """Greedy chain at the shape of the largest chain workload: B=256, gamma=7, V=152064, fp32."""
+    return chain_greedy_planted(seed, 256, 7, 152064, "f32", name="greedy_b256_g7_v152064_f32")
+
+
+def chain_greedy_b64_v128256(seed=7):
+    """Greedy chain at the shape of the Zipf workload: B=64, gamma=4, V=128256, bf16."""
+    return chain_greedy_planted(seed, 64, 4, 128256, "bf16", name="greedy_b64_g4_v128256_bf16")
+
+
 # ----------------------------------------------------------------------------- token trees
 
 def random_tree(gen, n_nodes, vocab, max_branch=4, max_depth=8):
@@ -367,3 +436,7 @@ CHAIN_WORKLOADS = {
     "gauss_b256_g7_v152064_f32": chain_b256_v152064,
 }
 TREE_WORKLOADS = {"tree_16x64_v32000_bf16": tree_16x64_v32000}
+GREEDY_WORKLOADS = {
+    "greedy_b256_g7_v152064_f32": chain_greedy_b256_v152064,
+    "greedy_b64_g4_v128256_bf16": chain_greedy_b64_v128256,
+}

@@ -18,6 +18,7 @@ import itertools
 import numpy as np
 
 from oracle import chain as OC
+from oracle import greedy as OG
 from oracle import tree as OT
 
 P_RTOL = 1e-5
@@ -122,3 +123,26 @@ def check_tree(batch, out, trees=None):
             assert [int(x) for x in out["node_argmax"][t]] == res["g"], f"tree {t}: argmax"
         accepted.append(k)
     return accepted
+
+
+def check_chain_greedy(batch, out, seqs=None):
+    """Compare GPU greedy chain outputs (numpy arrays) with the oracle, bit-exact.
+
+    out: dict with tokens [B, gamma+1], num_accepted [B], argmax [B, gamma+1] (or None),
+    status [B].  Returns the list of accepted counts.
+    """
+    B, gamma = batch.B, batch.gamma
+    seqs = range(B) if seqs is None else seqs
+    ks = []
+    for b in seqs:
+        res = OG.verify_chain_greedy_seq(OC.widen(batch.target[b], batch.dtype),
+                                         batch.draft_tokens[b])
+        want = res["tokens"] + [-1] * (gamma + 1 - len(res["tokens"]))
+        got = [int(x) for x in out["tokens"][b]]
+        assert int(out["num_accepted"][b]) == res["k"], (b, int(out["num_accepted"][b]), res)
+        assert got == want, (b, got, want)
+        assert int(out["status"][b]) == res["status"], (b, int(out["status"][b]), res["status"])
+        if out.get("argmax") is not None:
+            assert [int(x) for x in out["argmax"][b]] == res["g"], (b, out["argmax"][b], res["g"])
+        ks.append(res["k"])
+    return ks

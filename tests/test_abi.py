@@ -49,6 +49,9 @@ def test_workspace_sizes():
     g = lib.sv_verify_tree_workspace_bytes
     assert g(16, 64, 32000, BD.SV_BF16) >= 16 * 64 * 16 * 16
     assert g(16, 4097, 32000, BD.SV_BF16) == 0
+    h = lib.sv_verify_chain_greedy_workspace_bytes
+    assert h(256, 7, 152064, BD.SV_F32) >= 256 * 8 * 75 * 16
+    assert h(1, 65, 1000, BD.SV_F32) == 0 and h(0, 4, 1000, BD.SV_BF16) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
@@ -102,3 +105,25 @@ def test_tree_null_pointers(field):
 ])
 def test_tree_validation(kw, status):
     assert tree_call(**kw) == status
+
+
+def greedy_call(**kw):
+    a = dict(target=FAKE, dtype=BD.SV_BF16, toks=FAKE, B=2, gamma=4, V=1000, out_tokens=FAKE,
+             out_nacc=FAKE, out_g=None, out_status=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return BD.load().sv_verify_chain_greedy(*a.values())
+
+
+@pytest.mark.parametrize("field", ["target", "toks", "out_tokens", "out_nacc"])
+def test_greedy_null_pointers(field):
+    assert greedy_call(**{field: None}) == BD.SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), BD.SV_ERR_DTYPE),
+    (dict(B=0), BD.SV_ERR_SHAPE), (dict(gamma=0), BD.SV_ERR_SHAPE), (dict(gamma=65), BD.SV_ERR_SHAPE),
+    (dict(V=0), BD.SV_ERR_SHAPE), (dict(ws=None), BD.SV_ERR_WORKSPACE),
+    (dict(ws_bytes=16), BD.SV_ERR_WORKSPACE), (dict(ws=ctypes.c_void_p(0x1010)), BD.SV_ERR_WORKSPACE),
+])
+def test_greedy_host_validation(kw, status):
+    assert greedy_call(**kw) == status
