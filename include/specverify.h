@@ -180,6 +180,37 @@ sv_status sv_verify_chain_greedy(const void* target_logits, sv_dtype dtype,
                                  size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Per-position acceptance rates ([SpS] Step 3 accept probability, expected-speedup alpha, and
+ * the deployment section's monitoring of alpha): for each sequence b and position i < gamma,
+ *   alpha_i = sum_x q_i(x) min(1, p_i(x) / q_i(x)) = sum_x min(p_i(x), q_i(x)),
+ * the probability that a token drafted from q_i is accepted, with p_i, q_i the temperature
+ * softmaxes of target row i and draft row i as in sv_verify_chain.  Telemetry: it reads every
+ * target and draft row twice (softmax statistics, then the overlap), independently of any verify
+ * call.
+ *
+ * Arguments (device pointers, caller-owned, contiguous row-major):
+ *   target_logits  [B, gamma+1, V] of dtype (the layout of sv_verify_chain; row gamma is not read).
+ *   draft_logits   [B, gamma, V]   of dtype.
+ *   temperature    fp32 [B].
+ *   B in [1, 2^24], gamma in [1, 64], V in [1, 2^31 - 1].
+ *   out_alpha      fp32 [B, gamma]  (required)
+ *   out_status     int32 [B, gamma]: SV_ROW_* bits of each position (optional, NULL)
+ *   workspace      at least sv_chain_acceptance_rates_workspace_bytes(B, gamma, V, dtype)
+ *                  bytes, 256-byte aligned; no initialisation needed.
+ * A position whose target or draft row defines no softmax (NaN, +inf, only -inf) gets NaN and
+ * SV_ROW_NONFINITE; a temperature that is not finite and positive is replaced by 1 and sets
+ * SV_ROW_BAD_TEMPERATURE on every position of the sequence.
+ * ---------------------------------------------------------------------------------------- */
+size_t sv_chain_acceptance_rates_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
+                                                 sv_dtype dtype);
+
+sv_status sv_chain_acceptance_rates(const void* target_logits, const void* draft_logits,
+                                    sv_dtype dtype, const float* temperature, int32_t B,
+                                    int32_t gamma, int64_t V, float* out_alpha,
+                                    int32_t* out_status, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Kernel timing (measurement support; not part of the verify step).
  *
  * sv_trace_start(capacity): from now on, each kernel the library launches (up to `capacity`

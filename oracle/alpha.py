@@ -25,12 +25,12 @@ from .chain import ROW_BAD_TEMPERATURE, ROW_NONFINITE, row_is_valid, softmax_fp6
 
 
 def acceptance_rate(p, q):
-    """Expected Step-3 accept probability of a token drawn from q: sum_x q(x) min(1, p(x)/q(x))."""
-    out = 0.0
-    for px, qx in zip(p, q):
-        if qx > 0.0:
-            out += qx * min(1.0, px / qx)
-    return out
+    """Expected Step-3 accept probability of a token drawn from q: sum_x q(x) min(1, p(x)/q(x)),
+    over the tokens with q(x) > 0 (the others are never drafted)."""
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    drafted = q > 0.0
+    return float(np.sum(q[drafted] * np.minimum(1.0, p[drafted] / q[drafted])))
 
 
 def acceptance_rates_seq(target, draft, temperature):

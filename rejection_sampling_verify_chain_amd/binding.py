@@ -29,6 +29,7 @@ EXPORTS = (
     "sv_verify_chain_workspace_bytes", "sv_verify_chain",
     "sv_verify_tree_workspace_bytes", "sv_verify_tree",
     "sv_verify_chain_greedy_workspace_bytes", "sv_verify_chain_greedy",
+    "sv_chain_acceptance_rates_workspace_bytes", "sv_chain_acceptance_rates",
     "sv_trace_start", "sv_trace_stop", "sv_trace_kernels", "sv_trace_get",
 )
 
@@ -71,6 +72,11 @@ def load():
     lib.sv_verify_chain_greedy.restype = ctypes.c_int
     lib.sv_verify_chain_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i64,
                                            vp, vp, vp, vp, vp, sz, vp]
+    lib.sv_chain_acceptance_rates_workspace_bytes.restype = sz
+    lib.sv_chain_acceptance_rates_workspace_bytes.argtypes = [i32, i32, i64, ctypes.c_int]
+    lib.sv_chain_acceptance_rates.restype = ctypes.c_int
+    lib.sv_chain_acceptance_rates.argtypes = [vp, vp, ctypes.c_int, vp, i32, i32, i64,
+                                              vp, vp, vp, sz, vp]
     lib.sv_trace_start.restype = ctypes.c_int
     lib.sv_trace_start.argtypes = [ctypes.c_int]
     lib.sv_trace_stop.restype = ctypes.c_int
@@ -157,6 +163,10 @@ def tree_workspace_bytes(n_trees, n_nodes, V, dtype):
 
 def chain_greedy_workspace_bytes(B, gamma, V, dtype):
     return int(load().sv_verify_chain_greedy_workspace_bytes(B, gamma, V, _DTYPE[dtype]))
+
+
+def acceptance_rates_workspace_bytes(B, gamma, V, dtype):
+    return int(load().sv_chain_acceptance_rates_workspace_bytes(B, gamma, V, _DTYPE[dtype]))
 
 
 def workspace(nbytes, device):
@@ -276,6 +286,37 @@ def sv_verify_chain_greedy(target, draft_tokens, *, out_tokens=None, out_num_acc
         raise SpecVerifyError(st, "sv_verify_chain_greedy")
     return {"tokens": out_tokens, "num_accepted": out_num_accepted, "argmax": out_argmax,
             "status": out_status}
+
+
+def sv_chain_acceptance_rates(target, draft, temperature, *, out_alpha=None, out_status=None,
+                              workspace_buf=None, stream=None, want_status=True):
+    """Per-position acceptance rates through the C ABI.
+
+    target [B, gamma+1, V] and draft [B, gamma, V] (fp32 or bf16), temperature fp32 [B].
+    Returns a dict (alpha fp32 [B, gamma], status int32 [B, gamma]); the call is asynchronous.
+    """
+    lib = load()
+    if target.dtype not in _DTYPE:
+        raise ValueError(f"logits must be float32 or bfloat16, got {target.dtype}")
+    dev = target.device
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    _check(target, "target", None, (B, gamma + 1, V), dev)
+    _check(draft, "draft", target.dtype, (B, gamma, V), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    out_alpha = _out(out_alpha, "out_alpha", torch.float32, (B, gamma), dev)
+    if want_status or out_status is not None:
+        out_status = _out(out_status, "out_status", torch.int32, (B, gamma), dev)
+    need = acceptance_rates_workspace_bytes(B, gamma, V, target.dtype)
+    if workspace_buf is None:
+        workspace_buf = workspace(need, dev)
+    st = lib.sv_chain_acceptance_rates(
+        _ptr(target), _ptr(draft), _DTYPE[target.dtype], _ptr(temperature), B, gamma, V,
+        _ptr(out_alpha), _ptr(out_status), _ptr(workspace_buf), workspace_buf.numel(),
+        _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_chain_acceptance_rates")
+    return {"alpha": out_alpha, "status": out_status}
 
 
 # ----------------------------------------------------------------------------- host arrays

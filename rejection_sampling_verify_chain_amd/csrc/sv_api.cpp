@@ -43,6 +43,12 @@ bool greedy_shape_ok(int32_t B, int32_t gamma, int64_t V) {
   return grid_fits(B, gamma + 1, V);
 }
 
+bool alpha_shape_ok(int32_t B, int32_t gamma, int64_t V) {
+  if (B < 1 || B > sv::kMaxBatch || gamma < 1 || gamma > sv::kMaxGamma) return false;
+  if (V < 1 || V > int64_t(INT32_MAX)) return false;
+  return grid_fits(B, 2 * gamma, V);
+}
+
 }  // namespace
 
 SV_EXPORT const char* sv_version(void) { return "specverify 0.1.0 gfx950"; }
@@ -172,4 +178,38 @@ SV_EXPORT sv_status sv_verify_chain_greedy(const void* target_logits, sv_dtype d
   a.ws = static_cast<char*>(workspace);
   a.vec = aligned16(target_logits) && V % vec_width(dtype) == 0;
   return sv::launch_greedy(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+SV_EXPORT size_t sv_chain_acceptance_rates_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
+                                                           sv_dtype dtype) {
+  if (!valid_dtype(dtype) || !alpha_shape_ok(B, gamma, V)) return 0;
+  return sv::alpha_layout(B, gamma, V).total;
+}
+
+SV_EXPORT sv_status sv_chain_acceptance_rates(const void* target_logits, const void* draft_logits,
+                                              sv_dtype dtype, const float* temperature,
+                                              int32_t B, int32_t gamma, int64_t V,
+                                              float* out_alpha, int32_t* out_status,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  if (!target_logits || !draft_logits || !temperature || !out_alpha) return SV_ERR_NULL;
+  if (!valid_dtype(dtype)) return SV_ERR_DTYPE;
+  if (!alpha_shape_ok(B, gamma, V)) return SV_ERR_SHAPE;
+  const size_t need = sv::alpha_layout(B, gamma, V).total;
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SV_ERR_WORKSPACE;
+
+  sv::AlphaArgs a;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.dtype = dtype;
+  a.temperature = temperature;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.out_alpha = out_alpha;
+  a.out_status = out_status;
+  a.ws = static_cast<char*>(workspace);
+  a.vec = aligned16(target_logits) && aligned16(draft_logits) && V % vec_width(dtype) == 0;
+  return sv::launch_alpha(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

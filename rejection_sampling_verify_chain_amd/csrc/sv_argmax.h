@@ -24,7 +24,8 @@ __device__ __forceinline__ bool arg_better(float v, int32_t i, float bv, int32_t
 // flight together, then a butterfly reduction with the argmax order.
 constexpr int kMergeBatch = 4;
 
-__device__ __forceinline__ void merge_row_argmax(const ArgPart* pp, int64_t nchunk, int lane, int32_t* g, int* nan) {
+__device__ __forceinline__ void merge_row_argmax(const ArgPart* pp, int64_t nchunk, int lane,
+                                                 int32_t* g, int* nan) {
   float best = -INFINITY;
   int32_t bidx = INT32_MAX;
   int anynan = 0;

@@ -46,6 +46,8 @@ struct ChainParams {
   const float* uni;
   const float* temp;
   int gamma;
+  int tgt_rows;  // target rows per sequence the sweep covers: gamma + 1 (verify) or gamma
+
   int64_t V;
   int64_t nchunk;
   RowPart* part;
@@ -458,11 +460,13 @@ __global__ __launch_bounds__(kStreamBlock<T>, kStreamWavesPerSimd<VW>) void k_ch
   const int64_t gw = int64_t(blockIdx.x) * (kStreamBlock<T> / kWave) + wave_id();
   const T* tgt = static_cast<const T*>(p.tgt);
   const T* drf = static_cast<const T*>(p.drf);
+  // Row j of sequence b: target row j for j < tgt_rows, else draft row j - tgt_rows.
   stream_wave<RawChunk<T, VW>, kUnitsPerWave<T>>(
-      gw, total, p.nchunk, 2 * p.gamma + 1,
+      gw, total, p.nchunk, p.tgt_rows + p.gamma,
       [&](const Unit& k, RawChunk<T, VW>& r) {
-        load_raw<T, VW>(chain_row(tgt, drf, k.b, p.gamma, k.j, p.V) + int64_t(k.c) * kChunk,
-                        chunk_valid(p.V, k.c), lane, r);
+        const T* row = k.j < p.tgt_rows ? tgt + (k.b * (p.gamma + 1) + k.j) * p.V
+                                        : drf + (k.b * p.gamma + (k.j - p.tgt_rows)) * p.V;
+        load_raw<T, VW>(row + int64_t(k.c) * kChunk, chunk_valid(p.V, k.c), lane, r);
       },
       [&](const Unit& k, const RawChunk<T, VW>& r) {
         float z[kElemsPerLane];
@@ -518,6 +522,102 @@ __global__ __launch_bounds__(kWave) void k_chain_draw(ChainParams p) {
   draw_sequence<T, VW>(p, b, d);
 }
 
+// ------------------------------------------------------------------------------------ alpha
+
+// Acceptance rate alpha_i = sum_x min(p_i(x), q_i(x)) of position i of sequence b (the Step 3
+// accept probability averaged over x ~ q_i), one workgroup per (b, i).  Waves 0 and 1 merge the
+// chunk partials of target row i and draft row i; then every wave takes chunks c = wave,
+// wave + waves, ... and adds s * sum_x min(ra e_t(x), rb e_d(x)) for the chunk, where e_t, e_d
+// are the chunk-local softmax terms, A and B the chunk scales taking them to p and q,
+// s = max(A, B) and (ra, rb) = (A, B) / s (one of them is 1, the other at most 1, so nothing
+// overflows); the wave sums are added in wave order (deterministic).  The sweep that produced the
+// partials covered rows [target 0..gamma-1, draft 0..gamma-1] of every sequence.
+constexpr int kAlphaBlock = 512;
+constexpr int kAlphaWaves = kAlphaBlock / kWave;
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kAlphaBlock) void k_chain_alpha(ChainParams p, float* out_alpha,
+                                                            int32_t* out_status) {
+  __shared__ RowStat st[2];
+  __shared__ double wave_acc[kAlphaWaves];
+  const int gamma = p.gamma;
+  const int64_t b = blockIdx.x / gamma;
+  const int i = int(blockIdx.x - b * gamma);
+  const int R = 2 * gamma;
+  const int64_t nchunk = p.nchunk;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & (kWave - 1);
+  const float tb = p.temp[b];
+  const float te = effective_temperature(tb);
+  const double Td = te;
+  const float kk = log2e_over_t(te);
+  const RowPart* pt = p.part + (b * R + i) * nchunk;
+  const RowPart* pd = p.part + (b * R + gamma + i) * nchunk;
+  if (wave < 2) {
+    const RowStat s = merge_row(wave == 0 ? pt : pd, nchunk, lane, Td);
+    if (lane == 0) st[wave] = s;
+  }
+  __syncthreads();
+  const RowStat st_t = st[0], st_d = st[1];
+  const bool valid = st_t.valid && st_d.valid;
+  const T* zt_row = static_cast<const T*>(p.tgt) + (b * (gamma + 1) + i) * p.V;
+  const T* zd_row = static_cast<const T*>(p.drf) + (b * gamma + i) * p.V;
+  double acc = 0.0;
+  if (valid) {
+    for (int64_t c = wave; c < nchunk; c += kAlphaWaves) {
+      const RowPart ct = pt[c], cd = pd[c];
+      const double A = chunk_scale(ct.m, st_t, Td), Bq = chunk_scale(cd.m, st_d, Td);
+      if (A > 0.0 && Bq > 0.0) {  // wave-uniform; otherwise min(p, q) is 0 on the chunk
+        float zt[kElemsPerLane], zd[kElemsPerLane];
+        load_chunk<T, VW>(zt_row, p.V, c, lane, zt);
+        load_chunk<T, VW>(zd_row, p.V, c, lane, zd);
+        const double sc = fmax(A, Bq);
+        const float ra = float(A / sc), rb = float(Bq / sc);
+        acc += sc * wave_sum(lane_term_sum([&](int e) {
+                 return fminf(ra * softmax_term(zt[e], ct.m, kk),
+                              rb * softmax_term(zd[e], cd.m, kk));
+               }));
+      }
+    }
+  }
+  if (lane == 0) wave_acc[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double alpha = 0.0;
+    for (int w = 0; w < kAlphaWaves; ++w) alpha += wave_acc[w];
+    out_alpha[b * gamma + i] = valid ? float(alpha) : NAN;
+    if (out_status) {
+      int bits = valid ? 0 : SV_ROW_NONFINITE;
+      if (!(tb > 0.0f && tb < INFINITY)) bits |= SV_ROW_BAD_TEMPERATURE;
+      out_status[b * gamma + i] = bits;
+    }
+  }
+}
+
+template <typename T, int VW>
+hipError_t run_alpha(const AlphaArgs& a, hipStream_t s) {
+  const AlphaLayout L = alpha_layout(a.B, a.gamma, a.V);
+  ChainParams p = {};
+  p.tgt = a.target;
+  p.drf = a.draft;
+  p.temp = a.temperature;
+  p.gamma = a.gamma;
+  p.tgt_rows = a.gamma;
+  p.V = a.V;
+  p.nchunk = L.nchunk;
+  p.part = reinterpret_cast<RowPart*>(a.ws + L.off_part);
+  const int64_t total = int64_t(a.B) * (2 * a.gamma) * L.nchunk;
+  const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
+  constexpr int wpb = kStreamBlock<T> / kWave;
+  hipError_t e = launch_kernel("alpha_sweep", k_chain_sweep<T, VW>,
+                               dim3(unsigned((waves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
+                               p, total);
+  if (e != hipSuccess) return e;
+  return launch_kernel("alpha_overlap", k_chain_alpha<T, VW>,
+                       dim3(unsigned(int64_t(a.B) * a.gamma)), dim3(kAlphaBlock), s, p,
+                       a.out_alpha, a.out_status);
+}
+
 template <typename T, int VW>
 hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   const ChainLayout L = chain_layout(a.B, a.gamma, a.V);
@@ -528,6 +628,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   p.uni = a.uniforms;
   p.temp = a.temperature;
   p.gamma = a.gamma;
+  p.tgt_rows = a.gamma + 1;
   p.V = a.V;
   p.nchunk = L.nchunk;
   p.part = reinterpret_cast<RowPart*>(a.ws + L.off_part);
@@ -558,6 +659,11 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_alpha(const AlphaArgs& a, hipStream_t s) {
+  if (a.dtype == SV_F32) return a.vec ? run_alpha<float, 4>(a, s) : run_alpha<float, 1>(a, s);
+  return a.vec ? run_alpha<uint16_t, 8>(a, s) : run_alpha<uint16_t, 1>(a, s);
+}
 
 hipError_t launch_chain(const ChainArgs& a, hipStream_t s) {
   if (a.dtype == SV_F32) return a.vec ? run_chain<float, 4>(a, s) : run_chain<float, 1>(a, s);

@@ -117,6 +117,34 @@ inline GreedyLayout greedy_layout(int64_t B, int64_t gamma, int64_t V) {
   return L;
 }
 
+// Workspace of the acceptance-rate path: per (row, chunk) softmax partials of target rows
+// 0..gamma-1 and draft rows 0..gamma-1 of every sequence.
+struct AlphaLayout {
+  int64_t nchunk;
+  size_t off_part, total;
+};
+
+inline AlphaLayout alpha_layout(int64_t B, int64_t gamma, int64_t V) {
+  AlphaLayout L;
+  L.nchunk = n_chunks(V);
+  L.off_part = 0;
+  L.total = align256(sizeof(RowPart) * size_t(B) * size_t(2 * gamma) * size_t(L.nchunk));
+  return L;
+}
+
+struct AlphaArgs {
+  const void* target;
+  const void* draft;
+  sv_dtype dtype;
+  const float* temperature;
+  int32_t B, gamma;
+  int64_t V;
+  float* out_alpha;
+  int32_t* out_status;
+  char* ws;
+  bool vec;
+};
+
 struct ChainArgs {
   const void* target;
   const void* draft;
@@ -169,5 +197,6 @@ struct GreedyArgs {
 hipError_t launch_chain(const ChainArgs& a, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_greedy(const GreedyArgs& a, hipStream_t stream);
+hipError_t launch_alpha(const AlphaArgs& a, hipStream_t stream);
 
 }  // namespace sv

@@ -17,12 +17,17 @@ import itertools
 
 import numpy as np
 
+from oracle import alpha as OA
 from oracle import chain as OC
 from oracle import greedy as OG
 from oracle import tree as OT
 
 P_RTOL = 1e-5
 P_ATOL = 1e-30
+# Acceptance rates: |gpu - ref| <= 1e-5 * ref + 1e-12 (fp32 terms, fp64 sums; min is
+# 1-Lipschitz, so the terms' relative error carries over unamplified).
+ALPHA_RTOL = 1e-5
+ALPHA_ATOL = 1e-12
 
 
 def _neighbours(res):
@@ -146,3 +151,23 @@ def check_chain_greedy(batch, out, seqs=None):
             assert [int(x) for x in out["argmax"][b]] == res["g"], (b, out["argmax"][b], res["g"])
         ks.append(res["k"])
     return ks
+
+
+def check_acceptance_rates(batch, out, seqs=None):
+    """Compare GPU acceptance rates with the oracle: values within ALPHA_RTOL / ALPHA_ATOL (NaN
+    where the oracle gives NaN), status bits exact.  Returns the list of alpha arrays."""
+    seqs = range(batch.B) if seqs is None else seqs
+    res = []
+    for b in seqs:
+        al, st = OA.acceptance_rates_seq(OC.widen(batch.target[b], batch.dtype),
+                                         OC.widen(batch.draft[b], batch.dtype),
+                                         batch.temperature[b])
+        got = np.asarray(out["alpha"][b], dtype=np.float64)
+        nan = np.isnan(al)
+        assert np.array_equal(nan, np.isnan(got)), (b, got, al)
+        err = np.abs(got[~nan] - al[~nan])
+        assert np.all(err <= ALPHA_RTOL * al[~nan] + ALPHA_ATOL), (b, got, al, err)
+        if out.get("status") is not None:
+            assert [int(x) for x in out["status"][b]] == [int(x) for x in st], (b, out["status"][b], st)
+        res.append(al)
+    return res

@@ -49,6 +49,9 @@ def test_workspace_sizes():
     g = lib.sv_verify_tree_workspace_bytes
     assert g(16, 64, 32000, BD.SV_BF16) >= 16 * 64 * 16 * 16
     assert g(16, 4097, 32000, BD.SV_BF16) == 0
+    a = lib.sv_chain_acceptance_rates_workspace_bytes
+    assert a(256, 7, 152064, BD.SV_F32) >= 256 * 14 * 75 * 16
+    assert a(1, 65, 1000, BD.SV_F32) == 0 and a(1, 4, 1000, 9) == 0
     h = lib.sv_verify_chain_greedy_workspace_bytes
     assert h(256, 7, 152064, BD.SV_F32) >= 256 * 8 * 75 * 16
     assert h(1, 65, 1000, BD.SV_F32) == 0 and h(0, 4, 1000, BD.SV_BF16) == 0
@@ -127,3 +130,23 @@ def test_greedy_null_pointers(field):
 ])
 def test_greedy_host_validation(kw, status):
     assert greedy_call(**kw) == status
+
+
+def alpha_call(**kw):
+    a = dict(target=FAKE, draft=FAKE, dtype=BD.SV_F32, temp=FAKE, B=2, gamma=4, V=1000,
+             out_alpha=FAKE, out_status=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return BD.load().sv_chain_acceptance_rates(*a.values())
+
+
+@pytest.mark.parametrize("field", ["target", "draft", "temp", "out_alpha"])
+def test_alpha_null_pointers(field):
+    assert alpha_call(**{field: None}) == BD.SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), BD.SV_ERR_DTYPE), (dict(B=0), BD.SV_ERR_SHAPE), (dict(gamma=65), BD.SV_ERR_SHAPE),
+    (dict(V=-1), BD.SV_ERR_SHAPE), (dict(ws_bytes=0), BD.SV_ERR_WORKSPACE),
+])
+def test_alpha_host_validation(kw, status):
+    assert alpha_call(**kw) == status
