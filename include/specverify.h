@@ -23,6 +23,8 @@
  *         (gamma = look-ahead, temperature applied to both models).
  *  [SpI]  SpecInfer article (abeam.tech, arXiv:2305.09781): basic idea
  *         (基本アイデア) and inference (推論方法) — token-tree verification.
+ *  [SDE]  "投機的デコーディングとは？LLMの回答を高速化する仕組み"
+ *         (ai-compass.weeybrid.co.jp): 候補の採用と棄却を具体例で見る — greedy verification.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -209,6 +211,34 @@ sv_status sv_chain_acceptance_rates(const void* target_logits, const void* draft
                                     int32_t gamma, int64_t V, float* out_alpha,
                                     int32_t* out_status, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Draft-side sampler ([SpS] Step 1 and the code sketch's draft loop: each draft token is drawn
+ * from the softmax of the draft's logits divided by the temperature).
+ *
+ * For each row r: p = softmax(logits[r, :] / temperature[r]) and
+ *   out_tokens[r] = y = min{ x : sum_{t<=x} p(t) > uniforms[r] * sum_t p(t) }
+ * (inverse CDF in token-id order, the draw sv_verify_chain uses for its bonus token; a token of
+ * probability zero is never drawn); out_prob[r] = p(y).
+ *
+ * Arguments (device pointers, caller-owned):
+ *   logits       [rows, V] of dtype, contiguous rows.
+ *   temperature  fp32 [rows], finite and > 0.
+ *   uniforms     fp32 [rows] in [0, 1), drawn by the caller.
+ *   rows >= 1, V in [1, 2^31 - 1] (rows * ceil(V / 2048) / 4 below 2^31).
+ *   out_tokens   int32 [rows] (required)
+ *   out_prob     fp32 [rows]: p(y) (optional, NULL)
+ *   out_status   int32 [rows]: SV_ROW_* bits (optional, NULL)
+ *   workspace    at least sv_sample_workspace_bytes(rows, V, dtype) bytes, 256-byte aligned.
+ * A row with SV_ROW_NONFINITE, SV_ROW_BAD_TEMPERATURE or SV_ROW_BAD_UNIFORM takes token 0 and
+ * out_prob NaN.
+ * ---------------------------------------------------------------------------------------- */
+size_t sv_sample_workspace_bytes(int32_t rows, int64_t V, sv_dtype dtype);
+
+sv_status sv_sample(const void* logits, sv_dtype dtype, const float* temperature,
+                    const float* uniforms, int32_t rows, int64_t V, int32_t* out_tokens,
+                    float* out_prob, int32_t* out_status, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Kernel timing (measurement support; not part of the verify step).

@@ -30,6 +30,7 @@ EXPORTS = (
     "sv_verify_tree_workspace_bytes", "sv_verify_tree",
     "sv_verify_chain_greedy_workspace_bytes", "sv_verify_chain_greedy",
     "sv_chain_acceptance_rates_workspace_bytes", "sv_chain_acceptance_rates",
+    "sv_sample_workspace_bytes", "sv_sample",
     "sv_trace_start", "sv_trace_stop", "sv_trace_kernels", "sv_trace_get",
 )
 
@@ -77,6 +78,10 @@ def load():
     lib.sv_chain_acceptance_rates.restype = ctypes.c_int
     lib.sv_chain_acceptance_rates.argtypes = [vp, vp, ctypes.c_int, vp, i32, i32, i64,
                                               vp, vp, vp, sz, vp]
+    lib.sv_sample_workspace_bytes.restype = sz
+    lib.sv_sample_workspace_bytes.argtypes = [i32, i64, ctypes.c_int]
+    lib.sv_sample.restype = ctypes.c_int
+    lib.sv_sample.argtypes = [vp, ctypes.c_int, vp, vp, i32, i64, vp, vp, vp, vp, sz, vp]
     lib.sv_trace_start.restype = ctypes.c_int
     lib.sv_trace_start.argtypes = [ctypes.c_int]
     lib.sv_trace_stop.restype = ctypes.c_int
@@ -167,6 +172,10 @@ def chain_greedy_workspace_bytes(B, gamma, V, dtype):
 
 def acceptance_rates_workspace_bytes(B, gamma, V, dtype):
     return int(load().sv_chain_acceptance_rates_workspace_bytes(B, gamma, V, _DTYPE[dtype]))
+
+
+def sample_workspace_bytes(rows, V, dtype):
+    return int(load().sv_sample_workspace_bytes(rows, V, _DTYPE[dtype]))
 
 
 def workspace(nbytes, device):
@@ -319,6 +328,37 @@ def sv_chain_acceptance_rates(target, draft, temperature, *, out_alpha=None, out
     return {"alpha": out_alpha, "status": out_status}
 
 
+def sv_sample(logits, temperature, uniforms, *, out_tokens=None, out_prob=None, out_status=None,
+              workspace_buf=None, stream=None, want_prob=True, want_status=True):
+    """Draft-side sampler through the C ABI.
+
+    logits [rows, V] (fp32 or bf16), temperature and uniforms fp32 [rows].  Returns a dict
+    (tokens, prob, status); the call is asynchronous.
+    """
+    lib = load()
+    if logits.dtype not in _DTYPE:
+        raise ValueError(f"logits must be float32 or bfloat16, got {logits.dtype}")
+    dev = logits.device
+    rows, V = logits.shape
+    _check(logits, "logits", None, (rows, V), dev)
+    _check(temperature, "temperature", torch.float32, (rows,), dev)
+    _check(uniforms, "uniforms", torch.float32, (rows,), dev)
+    out_tokens = _out(out_tokens, "out_tokens", torch.int32, (rows,), dev)
+    if want_prob or out_prob is not None:
+        out_prob = _out(out_prob, "out_prob", torch.float32, (rows,), dev)
+    if want_status or out_status is not None:
+        out_status = _out(out_status, "out_status", torch.int32, (rows,), dev)
+    need = sample_workspace_bytes(rows, V, logits.dtype)
+    if workspace_buf is None:
+        workspace_buf = workspace(need, dev)
+    st = lib.sv_sample(_ptr(logits), _DTYPE[logits.dtype], _ptr(temperature), _ptr(uniforms), rows,
+                       V, _ptr(out_tokens), _ptr(out_prob), _ptr(out_status),
+                       _ptr(workspace_buf), workspace_buf.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_sample")
+    return {"tokens": out_tokens, "prob": out_prob, "status": out_status}
+
+
 # ----------------------------------------------------------------------------- host arrays
 
 def chain_to_device(batch, device="cuda"):
@@ -344,6 +384,15 @@ def greedy_to_device(batch, device="cuda"):
     t = t.view(torch.bfloat16) if batch.dtype == "bf16" else t
     return {"target": t.to(device),
             "draft_tokens": torch.from_numpy(batch.draft_tokens).to(device)}
+
+
+def sample_to_device(batch, device="cuda"):
+    """Copy a SampleBatch to device tensors."""
+    t = torch.from_numpy(batch.logits.view(np.int16) if batch.dtype == "bf16" else batch.logits)
+    t = t.view(torch.bfloat16) if batch.dtype == "bf16" else t
+    return {"logits": t.to(device),
+            "temperature": torch.from_numpy(batch.temperature).to(device),
+            "uniforms": torch.from_numpy(batch.uniforms).to(device)}
 
 
 def tree_to_device(batch, device="cuda"):

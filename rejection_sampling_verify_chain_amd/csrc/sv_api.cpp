@@ -49,6 +49,11 @@ bool alpha_shape_ok(int32_t B, int32_t gamma, int64_t V) {
   return grid_fits(B, 2 * gamma, V);
 }
 
+bool sample_shape_ok(int32_t rows, int64_t V) {
+  if (rows < 1 || V < 1 || V > int64_t(INT32_MAX)) return false;
+  return grid_fits(rows, 1, V);
+}
+
 }  // namespace
 
 SV_EXPORT const char* sv_version(void) { return "specverify 0.1.0 gfx950"; }
@@ -212,4 +217,35 @@ SV_EXPORT sv_status sv_chain_acceptance_rates(const void* target_logits, const v
   a.ws = static_cast<char*>(workspace);
   a.vec = aligned16(target_logits) && aligned16(draft_logits) && V % vec_width(dtype) == 0;
   return sv::launch_alpha(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+SV_EXPORT size_t sv_sample_workspace_bytes(int32_t rows, int64_t V, sv_dtype dtype) {
+  if (!valid_dtype(dtype) || !sample_shape_ok(rows, V)) return 0;
+  return sv::sample_layout(rows, V).total;
+}
+
+SV_EXPORT sv_status sv_sample(const void* logits, sv_dtype dtype, const float* temperature,
+                              const float* uniforms, int32_t rows, int64_t V,
+                              int32_t* out_tokens, float* out_prob, int32_t* out_status,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!logits || !temperature || !uniforms || !out_tokens) return SV_ERR_NULL;
+  if (!valid_dtype(dtype)) return SV_ERR_DTYPE;
+  if (!sample_shape_ok(rows, V)) return SV_ERR_SHAPE;
+  const size_t need = sv::sample_layout(rows, V).total;
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SV_ERR_WORKSPACE;
+
+  sv::SampleArgs a;
+  a.logits = logits;
+  a.dtype = dtype;
+  a.temperature = temperature;
+  a.uniforms = uniforms;
+  a.rows = rows;
+  a.V = V;
+  a.out_tokens = out_tokens;
+  a.out_prob = out_prob;
+  a.out_status = out_status;
+  a.ws = static_cast<char*>(workspace);
+  a.vec = aligned16(logits) && V % vec_width(dtype) == 0;
+  return sv::launch_sample(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

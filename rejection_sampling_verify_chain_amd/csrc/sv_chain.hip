@@ -618,6 +618,78 @@ hipError_t run_alpha(const AlphaArgs& a, hipStream_t s) {
                        a.out_alpha, a.out_status);
 }
 
+// ------------------------------------------------------------------------------------ sampler
+
+// Draft-side sampler, one wave per logit row r: merges the row's chunk partials into (M, S),
+// locates the chunk holding u * W from the chunk masses and rescans it in token order (the
+// inverse CDF of the bonus draw), and evaluates p(y) in fp64.  Rows with a bad temperature,
+// a bad uniform or no softmax take token 0.
+template <typename T, int VW>
+__global__ __launch_bounds__(kWave) void k_sample_draw(ChainParams p, const float* uni,
+                                                      int32_t* out_tokens, float* out_prob,
+                                                      int32_t* out_status) {
+  const int64_t r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t V = p.V, nchunk = p.nchunk;
+  const T* row = static_cast<const T*>(p.tgt) + r * V;
+  const float tb = p.temp[r];
+  const float te = effective_temperature(tb);
+  const double Td = te;
+  const float kk = log2e_over_t(te);
+  const RowPart* pp = p.part + r * nchunk;
+  const RowStat st = merge_row(pp, nchunk, lane, Td);
+  const float uf = uni[r];
+  int status = 0;
+  if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
+  if (!(uf >= 0.0f && uf < 1.0f)) status |= SV_ROW_BAD_UNIFORM;
+  if (!st.valid) status |= SV_ROW_NONFINITE;
+  int64_t y = 0;
+  double prob = NAN;
+  if (status == 0) {
+    const double u = uf;
+    const Located at = locate_chunk(nchunk, lane, u, [&](int64_t c) {
+      const RowPart q = pp[c];
+      return q.s * chunk_scale(q.m, st, Td);
+    });
+    const RowPart pc = pp[at.chunk];
+    const double scale = chunk_scale(pc.m, st, Td);
+    float z[kElemsPerLane];
+    load_chunk<T, VW>(row, V, at.chunk, lane, z);
+    const double tau_loc = scale > 0.0 ? (u * at.total - at.before) / scale : 0.0;
+    y = chunk_scan<VW>(at.chunk, V, lane, tau_loc,
+                       [&](int i) { return double(softmax_term(z[i], pc.m, kk)); });
+    prob = exp((double(widen(row[y])) - double(st.m)) / Td) / st.s;
+  }
+  if (lane == 0) {
+    out_tokens[r] = int32_t(y);
+    if (out_prob) out_prob[r] = float(prob);
+    if (out_status) out_status[r] = status;
+  }
+}
+
+template <typename T, int VW>
+hipError_t run_sample(const SampleArgs& a, hipStream_t s) {
+  const SampleLayout L = sample_layout(a.rows, a.V);
+  ChainParams p = {};
+  p.tgt = a.logits;
+  p.drf = a.logits;
+  p.temp = a.temperature;
+  p.gamma = 0;
+  p.tgt_rows = 1;
+  p.V = a.V;
+  p.nchunk = L.nchunk;
+  p.part = reinterpret_cast<RowPart*>(a.ws + L.off_part);
+  const int64_t total = int64_t(a.rows) * L.nchunk;
+  const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
+  constexpr int wpb = kStreamBlock<T> / kWave;
+  hipError_t e = launch_kernel("sample_sweep", k_chain_sweep<T, VW>,
+                               dim3(unsigned((waves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
+                               p, total);
+  if (e != hipSuccess) return e;
+  return launch_kernel("sample_draw", k_sample_draw<T, VW>, dim3(unsigned(a.rows)), dim3(kWave),
+                       s, p, a.uniforms, a.out_tokens, a.out_prob, a.out_status);
+}
+
 template <typename T, int VW>
 hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   const ChainLayout L = chain_layout(a.B, a.gamma, a.V);
@@ -659,6 +731,11 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
+  if (a.dtype == SV_F32) return a.vec ? run_sample<float, 4>(a, s) : run_sample<float, 1>(a, s);
+  return a.vec ? run_sample<uint16_t, 8>(a, s) : run_sample<uint16_t, 1>(a, s);
+}
 
 hipError_t launch_alpha(const AlphaArgs& a, hipStream_t s) {
   if (a.dtype == SV_F32) return a.vec ? run_alpha<float, 4>(a, s) : run_alpha<float, 1>(a, s);

@@ -145,6 +145,34 @@ struct AlphaArgs {
   bool vec;
 };
 
+// Workspace of the sampler: per (row, chunk) softmax partials.
+struct SampleLayout {
+  int64_t nchunk;
+  size_t off_part, total;
+};
+
+inline SampleLayout sample_layout(int64_t rows, int64_t V) {
+  SampleLayout L;
+  L.nchunk = n_chunks(V);
+  L.off_part = 0;
+  L.total = align256(sizeof(RowPart) * size_t(rows) * size_t(L.nchunk));
+  return L;
+}
+
+struct SampleArgs {
+  const void* logits;
+  sv_dtype dtype;
+  const float* temperature;
+  const float* uniforms;
+  int32_t rows;
+  int64_t V;
+  int32_t* out_tokens;
+  float* out_prob;
+  int32_t* out_status;
+  char* ws;
+  bool vec;
+};
+
 struct ChainArgs {
   const void* target;
   const void* draft;
@@ -198,5 +226,6 @@ hipError_t launch_chain(const ChainArgs& a, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_greedy(const GreedyArgs& a, hipStream_t stream);
 hipError_t launch_alpha(const AlphaArgs& a, hipStream_t stream);
+hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 
 }  // namespace sv

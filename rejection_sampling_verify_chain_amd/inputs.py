@@ -356,6 +356,60 @@ def chain_greedy_b64_v128256(seed=7):
     return chain_greedy_planted(seed, 64, 4, 128256, "bf16", name="greedy_b64_g4_v128256_bf16")
 
 
+# ----------------------------------------------------------------------------- sampler rows
+
+@dataclass
+class SampleBatch:
+    """One batch of sampler inputs: logits [rows, V] (fp32 or bf16 bit patterns), a temperature
+    and a uniform per row."""
+    name: str
+    dtype: str
+    logits: np.ndarray
+    temperature: np.ndarray
+    uniforms: np.ndarray
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self):
+        return self.logits.shape[0]
+
+    @property
+    def V(self):
+        return self.logits.shape[1]
+
+    @property
+    def logit_bytes(self):
+        return self.logits.nbytes
+
+
+def sample_gaussian(seed, rows, V, dtype, sigma, temperature, name=None):
+    """Sampler workload: logits ~ N(0, sigma^2) i.i.d.; temperature a scalar or per-row array;
+    uniforms on the 2^-24 grid."""
+    s_z, s_u = _streams(seed, 2)
+    z = np.empty((rows, V), dtype=np.float32)
+
+    def fill(g, r0, r1):
+        z[r0:r1] = g.standard_normal((r1 - r0, V), dtype=np.float32) * np.float32(sigma)
+
+    _fill_rows(s_z, rows, max(1, (1 << 22) // max(V, 1)), fill)
+    temp = np.broadcast_to(np.asarray(temperature, dtype=np.float32), (rows,)).copy()
+    u = uniforms(np.random.default_rng(s_u), (rows,))
+    return SampleBatch(name or f"sample_R{rows}_V{V}_{dtype}", dtype, _store(z, dtype), temp, u,
+                       {"sigma": sigma, "seed": seed})
+
+
+def sample_b256_v152064(seed=8):
+    """One draft token for each of 256 sequences, V=152064, fp32, T in {0.6, 1.0} per row."""
+    s_main, s_temp = _streams(seed, 2)
+    temp = np.where(np.random.default_rng(s_temp).random(256) < 0.5, 0.6, 1.0)
+    return sample_gaussian(s_main, 256, 152064, "f32", 2.5, temp, name="sample_b256_v152064_f32")
+
+
+def sample_b64_v128256(seed=9):
+    """One draft token for each of 64 sequences, V=128256, bf16, T=1."""
+    return sample_gaussian(seed, 64, 128256, "bf16", 2.5, 1.0, name="sample_b64_v128256_bf16")
+
+
 # ----------------------------------------------------------------------------- token trees
 
 def random_tree(gen, n_nodes, vocab, max_branch=4, max_depth=8):
@@ -436,6 +490,10 @@ CHAIN_WORKLOADS = {
     "gauss_b256_g7_v152064_f32": chain_b256_v152064,
 }
 TREE_WORKLOADS = {"tree_16x64_v32000_bf16": tree_16x64_v32000}
+SAMPLE_WORKLOADS = {
+    "sample_b256_v152064_f32": sample_b256_v152064,
+    "sample_b64_v128256_bf16": sample_b64_v128256,
+}
 GREEDY_WORKLOADS = {
     "greedy_b256_g7_v152064_f32": chain_greedy_b256_v152064,
     "greedy_b64_g4_v128256_bf16": chain_greedy_b64_v128256,

@@ -20,6 +20,7 @@ import numpy as np
 from oracle import alpha as OA
 from oracle import chain as OC
 from oracle import greedy as OG
+from oracle import sample as OS
 from oracle import tree as OT
 
 P_RTOL = 1e-5
@@ -171,3 +172,32 @@ def check_acceptance_rates(batch, out, seqs=None):
             assert [int(x) for x in out["status"][b]] == [int(x) for x in st], (b, out["status"][b], st)
         res.append(al)
     return res
+
+
+def check_sample(batch, out, rows=None):
+    """Compare GPU sampler outputs with the oracle: tokens bit-exact unless the oracle reports the
+    draw within the 1e-6 band of a bucket edge (then the oracle's token or the nearest
+    positive-weight token across that edge), p(y) within the probability bound, status exact.
+    Returns {"exact": n, "edge_band": n, "fallback": n}."""
+    rows = range(batch.rows) if rows is None else rows
+    counts = {"exact": 0, "edge_band": 0, "fallback": 0}
+    for r in rows:
+        res = OS.sample_row(OC.widen(batch.logits[r], batch.dtype), batch.temperature[r],
+                            batch.uniforms[r])
+        y = int(out["tokens"][r])
+        assert int(out["status"][r]) == res["status"], (r, int(out["status"][r]), res["status"])
+        if res["status"]:
+            assert y == 0, (r, y)
+            counts["fallback"] += 1
+            continue
+        if res["edge"] < OC.BAND:
+            allowed = _neighbours({"tokens": [res["token"]], "weights": res["weights"]})
+            assert y in allowed, (r, y, allowed)
+            counts["edge_band"] += 1
+        else:
+            assert y == res["token"], (r, y, res["token"])
+            counts["exact"] += 1
+        if out.get("prob") is not None:
+            ref = float(res["weights"][y])
+            assert abs(float(out["prob"][r]) - ref) <= P_RTOL * ref + P_ATOL, (r, out["prob"][r], ref)
+    return counts

@@ -52,6 +52,9 @@ def test_workspace_sizes():
     a = lib.sv_chain_acceptance_rates_workspace_bytes
     assert a(256, 7, 152064, BD.SV_F32) >= 256 * 14 * 75 * 16
     assert a(1, 65, 1000, BD.SV_F32) == 0 and a(1, 4, 1000, 9) == 0
+    sm = lib.sv_sample_workspace_bytes
+    assert sm(256, 152064, BD.SV_F32) >= 256 * 75 * 16
+    assert sm(0, 1000, BD.SV_F32) == 0 and sm(4, 0, BD.SV_BF16) == 0
     h = lib.sv_verify_chain_greedy_workspace_bytes
     assert h(256, 7, 152064, BD.SV_F32) >= 256 * 8 * 75 * 16
     assert h(1, 65, 1000, BD.SV_F32) == 0 and h(0, 4, 1000, BD.SV_BF16) == 0
@@ -150,3 +153,23 @@ def test_alpha_null_pointers(field):
 ])
 def test_alpha_host_validation(kw, status):
     assert alpha_call(**kw) == status
+
+
+def sample_call(**kw):
+    a = dict(logits=FAKE, dtype=BD.SV_BF16, temp=FAKE, uni=FAKE, rows=3, V=1000, out_tokens=FAKE,
+             out_prob=None, out_status=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return BD.load().sv_sample(*a.values())
+
+
+@pytest.mark.parametrize("field", ["logits", "temp", "uni", "out_tokens"])
+def test_sample_null_pointers(field):
+    assert sample_call(**{field: None}) == BD.SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=4), BD.SV_ERR_DTYPE), (dict(rows=0), BD.SV_ERR_SHAPE), (dict(V=0), BD.SV_ERR_SHAPE),
+    (dict(ws=None), BD.SV_ERR_WORKSPACE), (dict(ws_bytes=8), BD.SV_ERR_WORKSPACE),
+])
+def test_sample_host_validation(kw, status):
+    assert sample_call(**kw) == status
