@@ -23,6 +23,8 @@ Sources (cited by page title and section throughout):
 * Per-position acceptance rates (oracle/alpha.py): the Speculative Sampling explainer's
   Step 3 accept probability averaged over the drafted token.
 * The draft-side sampler (oracle/sample.py): Step 1 and the code sketch's draft loop.
+* Accepted-path KV compaction (oracle/kv.py): the explainer's KV-cache rollback note and
+  SpecInfer's append of the verified run.
 
 Pins: every function here is checked by the CPU tests against facts that do not
 come from this package (Theorem 1 by chi-square, the closed form for the
@@ -39,3 +41,4 @@ from .tree import argmax_first, verify_tree_one, verify_tree_batch  # noqa: F401
 from .greedy import verify_chain_greedy_seq, verify_chain_greedy_batch  # noqa: F401
 from .alpha import acceptance_rate, acceptance_rates_seq, acceptance_rates_batch  # noqa: F401
 from .sample import sample_row, sample_batch  # noqa: F401
+from .kv import ROW_BAD_INDEX, compact_one, compact_batch  # noqa: F401
