@@ -58,7 +58,8 @@ enum {
   SV_ROW_RESIDUAL_ZERO = 4,   /* rejection with zero residual mass: drawn from p_k instead     */
   SV_ROW_BAD_TREE = 8,        /* parents[0] != -1 or parents[i] not in [0, i)                  */
   SV_ROW_BAD_TEMPERATURE = 16,/* temperature not finite and > 0                               */
-  SV_ROW_BAD_UNIFORM = 32     /* a uniform outside [0, 1)                                      */
+  SV_ROW_BAD_UNIFORM = 32,    /* a uniform outside [0, 1)                                      */
+  SV_ROW_BAD_INDEX = 64       /* KV compaction: a path entry, count or destination out of range */
 };
 
 /* Library version string, e.g. "specverify 0.1.0 gfx950". */
@@ -239,6 +240,36 @@ sv_status sv_sample(const void* logits, sv_dtype dtype, const float* temperature
                     const float* uniforms, int32_t rows, int64_t V, int32_t* out_tokens,
                     float* out_prob, int32_t* out_status, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Accepted-path KV compaction ([SpS] implementation notes, KV cache management: the cache
+ * entries of rejected tokens are rolled back; [SpI] inference: the verified run is appended to
+ * the sequence).
+ *
+ * The verification pass computed one KV row per speculated position, including the position
+ * that feeds the first draft (a chain's last committed token, a tree's root): row u of sequence
+ * b's block belongs to node u (chain position u).  For each sequence b with k = num_accepted[b]:
+ *   for j = 0..k:  dst row (dst_start[b] + j) of sequence b  <-  src row path[b][j] of sequence b
+ * with path[b][j] = j when path is NULL (a chain).  Rows of rejected nodes are not read.  The
+ * path and count are those sv_verify_tree (out_path, out_num_accepted) or sv_verify_chain /
+ * sv_verify_chain_greedy (out_num_accepted, path NULL) return.
+ *
+ * Arguments (device pointers, caller-owned):
+ *   src           bytes [n, src_rows, row_bytes]: each sequence's speculative KV block.
+ *   dst           bytes [n, dst_rows, row_bytes]: each sequence's cache; must not overlap src.
+ *   row_bytes     bytes per KV row (all layers, keys and values, of one position), >= 1.
+ *   path          int32 [n, path_len] node ids (-1 padded), or NULL for chains.
+ *   num_accepted  int32 [n]; dst_start int32 [n]: first destination row of each sequence.
+ *   out_status    int32 [n]: SV_ROW_BAD_INDEX or 0 (optional, NULL).
+ * A sequence with k outside [0, path_len - 1] (src_rows - 1 without a path), a path entry outside
+ * [0, src_rows), or dst_start[b] + k + 1 > dst_rows sets SV_ROW_BAD_INDEX and copies nothing.
+ * Overlapping src and dst ranges return SV_ERR_SHAPE.  No workspace.  Rows use 16-byte accesses
+ * when src, dst and row_bytes are multiples of 16.
+ * ---------------------------------------------------------------------------------------- */
+sv_status sv_compact_accepted(const void* src, void* dst, int64_t row_bytes, int32_t n,
+                              int32_t src_rows, int32_t dst_rows, const int32_t* path,
+                              int32_t path_len, const int32_t* num_accepted,
+                              const int32_t* dst_start, int32_t* out_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Kernel timing (measurement support; not part of the verify step).

@@ -23,6 +23,7 @@ SV_F32, SV_BF16 = 0, 1
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_LAUNCH = 0, 1, 2, 3, 5, 6
 ROW_TOKEN_RANGE, ROW_NONFINITE, ROW_RESIDUAL_ZERO = 1, 2, 4
 ROW_BAD_TREE, ROW_BAD_TEMPERATURE, ROW_BAD_UNIFORM = 8, 16, 32
+ROW_BAD_INDEX = 64
 
 EXPORTS = (
     "sv_version", "sv_status_string",
@@ -31,6 +32,7 @@ EXPORTS = (
     "sv_verify_chain_greedy_workspace_bytes", "sv_verify_chain_greedy",
     "sv_chain_acceptance_rates_workspace_bytes", "sv_chain_acceptance_rates",
     "sv_sample_workspace_bytes", "sv_sample",
+    "sv_compact_accepted",
     "sv_trace_start", "sv_trace_stop", "sv_trace_kernels", "sv_trace_get",
 )
 
@@ -82,6 +84,8 @@ def load():
     lib.sv_sample_workspace_bytes.argtypes = [i32, i64, ctypes.c_int]
     lib.sv_sample.restype = ctypes.c_int
     lib.sv_sample.argtypes = [vp, ctypes.c_int, vp, vp, i32, i64, vp, vp, vp, vp, sz, vp]
+    lib.sv_compact_accepted.restype = ctypes.c_int
+    lib.sv_compact_accepted.argtypes = [vp, vp, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp]
     lib.sv_trace_start.restype = ctypes.c_int
     lib.sv_trace_start.argtypes = [ctypes.c_int]
     lib.sv_trace_stop.restype = ctypes.c_int
@@ -359,6 +363,35 @@ def sv_sample(logits, temperature, uniforms, *, out_tokens=None, out_prob=None, 
     return {"tokens": out_tokens, "prob": out_prob, "status": out_status}
 
 
+def sv_compact_accepted(src, dst, num_accepted, dst_start, path=None, *, out_status=None,
+                        stream=None, want_status=True):
+    """Accepted-path KV compaction through the C ABI.
+
+    src uint8 [n, src_rows, row_bytes], dst uint8 [n, dst_rows, row_bytes] (modified in place),
+    num_accepted and dst_start int32 [n], path int32 [n, path_len] or None (chains).  Returns a
+    dict (status); the call is asynchronous.
+    """
+    lib = load()
+    dev = src.device
+    n, src_rows, row_bytes = src.shape
+    _check(src, "src", torch.uint8, (n, src_rows, row_bytes), dev)
+    _check(dst, "dst", torch.uint8, (n, dst.shape[1], row_bytes), dev)
+    _check(num_accepted, "num_accepted", torch.int32, (n,), dev)
+    _check(dst_start, "dst_start", torch.int32, (n,), dev)
+    path_len = 0
+    if path is not None:
+        path_len = path.shape[1]
+        _check(path, "path", torch.int32, (n, path_len), dev)
+    if want_status or out_status is not None:
+        out_status = _out(out_status, "out_status", torch.int32, (n,), dev)
+    st = lib.sv_compact_accepted(_ptr(src), _ptr(dst), row_bytes, n, src_rows, dst.shape[1],
+                                 _ptr(path), path_len, _ptr(num_accepted), _ptr(dst_start),
+                                 _ptr(out_status), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_compact_accepted")
+    return {"status": out_status}
+
+
 # ----------------------------------------------------------------------------- host arrays
 
 def chain_to_device(batch, device="cuda"):
@@ -393,6 +426,15 @@ def sample_to_device(batch, device="cuda"):
     return {"logits": t.to(device),
             "temperature": torch.from_numpy(batch.temperature).to(device),
             "uniforms": torch.from_numpy(batch.uniforms).to(device)}
+
+
+def kv_to_device(batch, device="cuda"):
+    """Copy a KvBatch to device tensors (the destination starts as the batch's initial cache)."""
+    return {"src": torch.from_numpy(batch.src).to(device),
+            "dst": torch.from_numpy(batch.dst_init).to(device),
+            "path": None if batch.paths is None else torch.from_numpy(batch.paths).to(device),
+            "num_accepted": torch.from_numpy(batch.num_accepted).to(device),
+            "dst_start": torch.from_numpy(batch.dst_start).to(device)}
 
 
 def tree_to_device(batch, device="cuda"):

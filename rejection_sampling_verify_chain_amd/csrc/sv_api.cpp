@@ -249,3 +249,36 @@ SV_EXPORT sv_status sv_sample(const void* logits, sv_dtype dtype, const float* t
   a.vec = aligned16(logits) && V % vec_width(dtype) == 0;
   return sv::launch_sample(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
+
+SV_EXPORT sv_status sv_compact_accepted(const void* src, void* dst, int64_t row_bytes, int32_t n,
+                                        int32_t src_rows, int32_t dst_rows, const int32_t* path,
+                                        int32_t path_len, const int32_t* num_accepted,
+                                        const int32_t* dst_start, int32_t* out_status,
+                                        hipStream_t stream) {
+  if (!src || !dst || !num_accepted || !dst_start) return SV_ERR_NULL;
+  if (n < 1 || src_rows < 1 || dst_rows < 1 || row_bytes < 1) return SV_ERR_SHAPE;
+  if (path && path_len < 1) return SV_ERR_SHAPE;
+  const int64_t src_bytes = int64_t(n) * src_rows * row_bytes;
+  const int64_t dst_bytes = int64_t(n) * dst_rows * row_bytes;
+  // Grid: one block per (sequence, 8 path-slot groups, tile of at least 1 KiB); keep it within
+  // 32 bits.
+  const int64_t tiles = (row_bytes + 1023) / 1024;
+  if (row_bytes > (int64_t(1) << 40) || int64_t(n) * 8 * tiles >= int64_t(INT32_MAX))
+    return SV_ERR_SHAPE;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + uintptr_t(dst_bytes) && d0 < s0 + uintptr_t(src_bytes)) return SV_ERR_SHAPE;
+
+  sv::KvArgs a;
+  a.src = src;
+  a.dst = dst;
+  a.row_bytes = row_bytes;
+  a.n = n;
+  a.src_rows = src_rows;
+  a.dst_rows = dst_rows;
+  a.path = path;
+  a.path_len = path_len;
+  a.num_accepted = num_accepted;
+  a.dst_start = dst_start;
+  a.out_status = out_status;
+  return sv::launch_kv_compact(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}

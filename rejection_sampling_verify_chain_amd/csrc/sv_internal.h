@@ -173,6 +173,18 @@ struct SampleArgs {
   bool vec;
 };
 
+struct KvArgs {
+  const void* src;
+  void* dst;
+  int64_t row_bytes;
+  int32_t n, src_rows, dst_rows;
+  const int32_t* path;
+  int32_t path_len;
+  const int32_t* num_accepted;
+  const int32_t* dst_start;
+  int32_t* out_status;
+};
+
 struct ChainArgs {
   const void* target;
   const void* draft;
@@ -227,5 +239,6 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t stream);
 hipError_t launch_greedy(const GreedyArgs& a, hipStream_t stream);
 hipError_t launch_alpha(const AlphaArgs& a, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
+hipError_t launch_kv_compact(const KvArgs& a, hipStream_t stream);
 
 }  // namespace sv

@@ -410,6 +410,103 @@ def sample_b64_v128256(seed=9):
     return sample_gaussian(seed, 64, 128256, "bf16", 2.5, 1.0, name="sample_b64_v128256_bf16")
 
 
+# ----------------------------------------------------------------------------- KV blocks
+
+@dataclass
+class KvBatch:
+    """One batch of KV-compaction inputs: speculative KV blocks src [n, src_rows, row_bytes]
+    (uint8), the initial caches dst_init [n, dst_rows, row_bytes], accepted paths [n, path_len]
+    (node ids, -1 padded; None for chains), accepted counts and destination start rows."""
+    name: str
+    src: np.ndarray
+    dst_init: np.ndarray
+    paths: object
+    num_accepted: np.ndarray
+    dst_start: np.ndarray
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def n(self):
+        return self.src.shape[0]
+
+    @property
+    def row_bytes(self):
+        return self.src.shape[2]
+
+    @property
+    def moved_rows(self):
+        return int((self.num_accepted.astype(np.int64) + 1).sum())
+
+
+def _random_bytes(seq, shape):
+    out = np.empty(shape, dtype=np.uint8)
+    flat = out.reshape(shape[0] * shape[1], shape[2])
+
+    def fill(g, r0, r1):
+        flat[r0:r1] = g.integers(0, 256, size=(r1 - r0, shape[2]), dtype=np.uint8)
+
+    _fill_rows(seq, shape[0] * shape[1], max(1, (1 << 24) // max(shape[2], 1)), fill)
+    return out
+
+
+def kv_tree_paths(seed, n_trees, n_nodes, row_bytes, dst_rows=96, max_branch=4, max_depth=8,
+                  stop_prob=0.25, name=None):
+    """Tree KV workload: random BFS trees (as the tree workloads), and for each a synthetic
+    accepted path that starts at the root and moves to a uniformly chosen child until it reaches
+    a leaf or stops (probability stop_prob per step); random KV bytes; the cache's destination
+    starts at a random row leaving room for the path."""
+    s_tree, s_walk, s_src, s_dst = _streams(seed, 4)
+    gt = np.random.default_rng(s_tree)
+    gw = np.random.default_rng(s_walk)
+    paths = np.full((n_trees, n_nodes), -1, dtype=np.int32)
+    k = np.empty(n_trees, dtype=np.int32)
+    start = np.empty(n_trees, dtype=np.int32)
+    for t in range(n_trees):
+        parents, _ = random_tree(gt, n_nodes, 1000, max_branch, max_depth)
+        u, path = 0, [0]
+        while True:
+            kids = np.flatnonzero(parents == u)
+            if len(kids) == 0 or gw.random() < stop_prob:
+                break
+            u = int(kids[int(gw.integers(0, len(kids)))])
+            path.append(u)
+        paths[t, :len(path)] = path
+        k[t] = len(path) - 1
+        start[t] = int(gw.integers(0, dst_rows - len(path) + 1))
+    src = _random_bytes(s_src, (n_trees, n_nodes, row_bytes))
+    dst = _random_bytes(s_dst, (n_trees, dst_rows, row_bytes))
+    return KvBatch(name or f"kv_tree_{n_trees}x{n_nodes}_W{row_bytes}", src, dst, paths, k, start,
+                   {"seed": seed})
+
+
+def kv_chain(seed, B, gamma, row_bytes, dst_rows=64, name=None):
+    """Chain KV workload: gamma + 1 KV rows per sequence, a uniform accepted count in [0, gamma],
+    random KV bytes and destination start rows."""
+    s_k, s_src, s_dst = _streams(seed, 3)
+    g = np.random.default_rng(s_k)
+    k = g.integers(0, gamma + 1, size=B).astype(np.int32)
+    start = np.array([g.integers(0, dst_rows - kk) for kk in k], dtype=np.int32)
+    src = _random_bytes(s_src, (B, gamma + 1, row_bytes))
+    dst = _random_bytes(s_dst, (B, dst_rows, row_bytes))
+    return KvBatch(name or f"kv_chain_B{B}_g{gamma}_W{row_bytes}", src, dst, None, k, start,
+                   {"seed": seed})
+
+
+# Bytes of one token's KV row for a 32-layer model with 8 KV heads of dimension 128 in bf16
+# (keys and values): 32 * 2 * 8 * 128 * 2.
+KV_ROW_BYTES = 131072
+
+
+def kv_tree_16x64():
+    """KV rows of the 16 x 64-node token trees, 128 KiB per row, synthetic accepted paths."""
+    return kv_tree_paths(10, 16, 64, KV_ROW_BYTES, name="kv_tree_16x64_w131072")
+
+
+def kv_chain_b256_g7():
+    """KV rows of 256 chains of gamma = 7, 128 KiB per row, uniform accepted counts."""
+    return kv_chain(11, 256, 7, KV_ROW_BYTES, dst_rows=16, name="kv_chain_b256_g7_w131072")
+
+
 # ----------------------------------------------------------------------------- token trees
 
 def random_tree(gen, n_nodes, vocab, max_branch=4, max_depth=8):
@@ -493,6 +590,10 @@ TREE_WORKLOADS = {"tree_16x64_v32000_bf16": tree_16x64_v32000}
 SAMPLE_WORKLOADS = {
     "sample_b256_v152064_f32": sample_b256_v152064,
     "sample_b64_v128256_bf16": sample_b64_v128256,
+}
+KV_WORKLOADS = {
+    "kv_tree_16x64_w131072": kv_tree_16x64,
+    "kv_chain_b256_g7_w131072": kv_chain_b256_g7,
 }
 GREEDY_WORKLOADS = {
     "greedy_b256_g7_v152064_f32": chain_greedy_b256_v152064,

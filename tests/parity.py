@@ -20,6 +20,7 @@ import numpy as np
 from oracle import alpha as OA
 from oracle import chain as OC
 from oracle import greedy as OG
+from oracle import kv as OK
 from oracle import sample as OS
 from oracle import tree as OT
 
@@ -201,3 +202,13 @@ def check_sample(batch, out, rows=None):
             ref = float(res["weights"][y])
             assert abs(float(out["prob"][r]) - ref) <= P_RTOL * ref + P_ATOL, (r, out["prob"][r], ref)
     return counts
+
+
+def check_kv(batch, dst_out, status):
+    """GPU KV compaction against the oracle: the whole destination bytes exact, status exact."""
+    ref = batch.dst_init.copy()
+    st = OK.compact_batch(batch.src, ref, batch.paths, batch.num_accepted, batch.dst_start)
+    assert np.array_equal(np.asarray(status), st), (status, st)
+    for b in range(batch.n):
+        assert np.array_equal(dst_out[b], ref[b]), f"sequence {b}: destination bytes differ"
+    return st

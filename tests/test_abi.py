@@ -173,3 +173,23 @@ def test_sample_null_pointers(field):
 ])
 def test_sample_host_validation(kw, status):
     assert sample_call(**kw) == status
+
+
+def kv_call(**kw):
+    a = dict(src=ctypes.c_void_p(0x100000), dst=ctypes.c_void_p(0x900000), row_bytes=1024, n=2,
+             src_rows=8, dst_rows=16, path=None, path_len=0, k=FAKE, start=FAKE, status=None,
+             stream=None)
+    a.update(kw)
+    return BD.load().sv_compact_accepted(*a.values())
+
+
+@pytest.mark.parametrize("field", ["src", "dst", "k", "start"])
+def test_kv_null_pointers(field):
+    assert kv_call(**{field: None}) == BD.SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(n=0), dict(row_bytes=0), dict(src_rows=0), dict(dst_rows=0),
+                                dict(path=FAKE, path_len=0),
+                                dict(dst=ctypes.c_void_p(0x100000 + 4096))])  # overlaps src
+def test_kv_host_validation(kw):
+    assert kv_call(**kw) == BD.SV_ERR_SHAPE
