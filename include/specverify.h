@@ -275,7 +275,8 @@ sv_status sv_compact_accepted(const void* src, void* dst, int64_t row_bytes, int
  * Kernel timing (measurement support; not part of the verify step).
  *
  * sv_trace_start(capacity): from now on, each kernel the library launches (up to `capacity`
- *   launches in total) is bracketed by two HIP events recorded on its launch stream.  Creates
+ *   launches in total) is given two HIP events that the launch stamps with the start and end
+ *   of that kernel's execution on its stream (hipExtLaunchKernel's events).  Creates
  *   2*capacity HIP events (host-side objects; no device memory).  Returns 0, or -1 if event
  *   creation failed.  Calling it again discards earlier records.
  * sv_trace_stop(): stops recording; returns the number of launches recorded.

@@ -220,7 +220,8 @@ struct DecideShared {
 };
 
 // The decision for sequence b from the chunk partials of its rows.  Called by all threads of
-// the sequence's workgroup.
+// the sequence's workgroup.  Wave 0 first fetches the draft tokens and gathers the two logits
+// each one picks, so that those dependent loads overlap the partials' merge.
 template <typename T, int VW>
 __device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& sh) {
   const T* tgt = static_cast<const T*>(p.tgt);
@@ -230,8 +231,20 @@ __device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& s
   const int R = 2 * gamma + 1;
   const int wave = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
-  const float tb = p.temp[b];
+  const float tb = uniform_load(p.temp, b);
   const double Td = effective_temperature(tb);
+
+  int x = 0;
+  bool xbad = false;
+  float zt_x = 0.0f, zd_x = 0.0f;
+  if (wave == 0 && lane < gamma) {
+    x = p.toks[b * gamma + lane];
+    xbad = (x < 0) || (int64_t(x) >= V);
+    if (!xbad) {
+      zt_x = widen(chain_row(tgt, drf, b, gamma, lane, V)[x]);
+      zd_x = widen(chain_row(tgt, drf, b, gamma, gamma + 1 + lane, V)[x]);
+    }
+  }
 
   // Row max and normaliser of every row of the sequence, one wave per row.
   for (int j = wave; j < R; j += kWavesPerBlock) {
@@ -253,13 +266,7 @@ __device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& s
     bad |= !(u >= 0.0f && u < 1.0f);
   }
   if (__any(bad)) status |= SV_ROW_BAD_UNIFORM;
-  int x = 0;
-  bad = false;
-  if (lane < gamma) {
-    x = p.toks[b * gamma + lane];
-    bad = (x < 0) || (int64_t(x) >= V);
-  }
-  if (__any(bad)) status |= SV_ROW_TOKEN_RANGE;
+  if (__any(xbad)) status |= SV_ROW_TOKEN_RANGE;
   bad = false;
   for (int j = lane; j < R; j += kWave) bad |= !sh.st[j].valid;
   if (__any(bad)) status |= SV_ROW_NONFINITE;
@@ -272,10 +279,8 @@ __device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& s
     if (lane < gamma) {
       const RowStat a = sh.st[lane];
       const RowStat d = sh.st[gamma + 1 + lane];
-      const double zt = widen(chain_row(tgt, drf, b, gamma, lane, V)[x]);
-      const double zd = widen(chain_row(tgt, drf, b, gamma, gamma + 1 + lane, V)[x]);
-      const double pi = exp((zt - double(a.m)) / Td) / a.s;
-      const double qi = exp((zd - double(d.m)) / Td) / d.s;
+      const double pi = exp((double(zt_x) - double(a.m)) / Td) / a.s;
+      const double qi = exp((double(zd_x) - double(d.m)) / Td) / d.s;
       const double u = p.uni[b * (gamma + 1) + lane];
       if (qi > 0.0) {
         accept = u < fmin(1.0, pi / qi);
@@ -388,7 +393,10 @@ __device__ Located locate_chunk(int64_t nchunk, int lane, double u, MassFn mass)
 }
 
 // Draw of sequence b (one wave): residual draw over the residual chunk masses (falling back to
-// p_k if they sum to zero), or the bonus draw from p_gamma over the sweep's chunk masses.
+// p_k if they sum to zero), or the bonus draw from p_gamma over the sweep's chunk masses.  The
+// wave-uniform records (row statistics, the located chunk's partials, T, u) come through the
+// scalar cache, issued beside the vector loads they do not depend on, so the draw takes three
+// dependent memory round trips: the decision, the chunk masses, the located chunk.
 template <typename T, int VW>
 __device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision& d) {
   const T* tgt = static_cast<const T*>(p.tgt);
@@ -397,27 +405,33 @@ __device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision
   const int64_t V = p.V, nchunk = p.nchunk;
   const int R = 2 * gamma + 1;
   const int lane = threadIdx.x & (kWave - 1);
-  const float te = effective_temperature(p.temp[b]);
+  const float te = effective_temperature(uniform_load(p.temp, b));
   const double Td = te;
   const float kk = log2e_over_t(te);
   const int k = d.k;
   int status = d.status;
-  const double u = p.uni[b * (gamma + 1) + gamma];
+  const double u = uniform_load(p.uni, b * (gamma + 1) + gamma);
 
   int64_t y = -1;
   if (d.mode == kDrawResidual) {
+    const int jt = k, jd = gamma + 1 + k;
+    const RowStat st_t = uniform_load(p.rowstat, b * R + jt);
+    const RowStat st_d = uniform_load(p.rowstat, b * R + jd);
     const double* wr = p.wres + b * nchunk;
     const Located at = locate_chunk(nchunk, lane, u, [&](int64_t c) { return wr[c]; });
     if (at.total > 0.0) {
       const int64_t cs = at.chunk;
-      const int jt = k, jd = gamma + 1 + k;
-      const RowPart pt = p.part[(b * R + jt) * nchunk + cs];
-      const RowPart pd = p.part[(b * R + jd) * nchunk + cs];
-      const ResidualScale rs = residual_scale(chunk_scale(pt.m, p.rowstat[b * R + jt], Td),
-                                              chunk_scale(pd.m, p.rowstat[b * R + jd], Td));
+      const int nvalid = chunk_valid(V, cs);
+      RawChunk<T, VW> rt, rd;
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jt, V) + cs * kChunk, nvalid, lane, rt);
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jd, V) + cs * kChunk, nvalid, lane, rd);
+      const RowPart pt = uniform_load(p.part, (b * R + jt) * nchunk + cs);
+      const RowPart pd = uniform_load(p.part, (b * R + jd) * nchunk + cs);
+      const ResidualScale rs =
+          residual_scale(chunk_scale(pt.m, st_t, Td), chunk_scale(pd.m, st_d, Td));
       float zt[kElemsPerLane], zd[kElemsPerLane];
-      load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jt, V), V, cs, lane, zt);
-      load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jd, V), V, cs, lane, zd);
+      unpack_chunk<T, VW>(rt, nvalid, lane, zt);
+      unpack_chunk<T, VW>(rd, nvalid, lane, zd);
       const double tau_loc = rs.A > 0.0 ? (u * at.total - at.before) / rs.A : 0.0;
       y = chunk_scan<VW>(cs, V, lane, tau_loc, [&](int i) {
         return double(residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs));
@@ -429,17 +443,20 @@ __device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision
   if (y < 0) {
     // Bonus draw from p_gamma, or the zero-residual fallback from p_k.
     const int jr = d.mode == kDrawBonus ? gamma : k;
-    const RowStat srow = p.rowstat[b * R + jr];
+    const RowStat srow = uniform_load(p.rowstat, b * R + jr);
     const RowPart* pp = p.part + (b * R + jr) * nchunk;
     const Located at = locate_chunk(nchunk, lane, u, [&](int64_t c) {
       const RowPart q = pp[c];
       return q.s * chunk_scale(q.m, srow, Td);
     });
     const int64_t cs = at.chunk;
-    const RowPart pc = pp[cs];
+    const int nvalid = chunk_valid(V, cs);
+    RawChunk<T, VW> r;
+    load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jr, V) + cs * kChunk, nvalid, lane, r);
+    const RowPart pc = uniform_load(pp, cs);
     const double scale = chunk_scale(pc.m, srow, Td);
     float z[kElemsPerLane];
-    load_chunk<T, VW>(chain_row(tgt, drf, b, gamma, jr, V), V, cs, lane, z);
+    unpack_chunk<T, VW>(r, nvalid, lane, z);
     const double tau_loc = scale > 0.0 ? (u * at.total - at.before) / scale : 0.0;
     y = chunk_scan<VW>(cs, V, lane, tau_loc,
                        [&](int i) { return double(softmax_term(z[i], pc.m, kk)); });
@@ -483,6 +500,10 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(ChainParams p) {
   decide_sequence<T, VW>(p, blockIdx.x, sh);
 }
 
+// The wave's chunk loads of both rows are issued as soon as the decision (which row) is known;
+// the chunk partials and row statistics that scale them arrive through the scalar cache while
+// the chunk is in flight.  A chunk whose target part is all -inf (A = 0) is loaded too and adds
+// nothing.
 template <typename T, int VW>
 __global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p, int64_t total) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -490,34 +511,35 @@ __global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p
   if (w >= total) return;  // wave-uniform
   const int64_t b = w / p.nchunk;
   const int64_t c = w - b * p.nchunk;
-  const SeqDecision d = p.seq[b];
+  const SeqDecision d = uniform_load(p.seq, b);
   if (d.mode != kDrawResidual) return;
   const int R = 2 * p.gamma + 1;
   const int jt = d.k, jd = p.gamma + 1 + d.k;
   const T* tgt = static_cast<const T*>(p.tgt);
   const T* drf = static_cast<const T*>(p.drf);
-  const float te = effective_temperature(p.temp[b]);
+  const int nvalid = chunk_valid(p.V, c);
+  RawChunk<T, VW> rt, rd;
+  load_raw<T, VW>(chain_row(tgt, drf, b, p.gamma, jt, p.V) + c * kChunk, nvalid, lane, rt);
+  load_raw<T, VW>(chain_row(tgt, drf, b, p.gamma, jd, p.V) + c * kChunk, nvalid, lane, rd);
+  const float te = effective_temperature(uniform_load(p.temp, b));
   const double Td = te;
   const float kk = log2e_over_t(te);
-  const RowPart pt = p.part[(b * R + jt) * p.nchunk + c];
-  const RowPart pd = p.part[(b * R + jd) * p.nchunk + c];
-  const ResidualScale rs = residual_scale(chunk_scale(pt.m, p.rowstat[b * R + jt], Td),
-                                          chunk_scale(pd.m, p.rowstat[b * R + jd], Td));
-  double wsum = 0.0;
-  if (rs.A > 0.0) {  // wave-uniform
-    float zt[kElemsPerLane], zd[kElemsPerLane];
-    load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jt, p.V), p.V, c, lane, zt);
-    load_chunk<T, VW>(chain_row(tgt, drf, b, p.gamma, jd, p.V), p.V, c, lane, zd);
-    wsum = rs.A * wave_sum(lane_term_sum(
-                      [&](int i) { return residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs); }));
-  }
-  if (lane == 0) p.wres[w] = wsum;
+  const RowPart pt = uniform_load(p.part, (b * R + jt) * p.nchunk + c);
+  const RowPart pd = uniform_load(p.part, (b * R + jd) * p.nchunk + c);
+  const ResidualScale rs = residual_scale(chunk_scale(pt.m, uniform_load(p.rowstat, b * R + jt), Td),
+                                          chunk_scale(pd.m, uniform_load(p.rowstat, b * R + jd), Td));
+  float zt[kElemsPerLane], zd[kElemsPerLane];
+  unpack_chunk<T, VW>(rt, nvalid, lane, zt);
+  unpack_chunk<T, VW>(rd, nvalid, lane, zd);
+  const double wsum = wave_sum(lane_term_sum(
+      [&](int i) { return residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs); }));
+  if (lane == 0) p.wres[w] = rs.A > 0.0 ? rs.A * wsum : 0.0;
 }
 
 template <typename T, int VW>
 __global__ __launch_bounds__(kWave) void k_chain_draw(ChainParams p) {
   const int64_t b = blockIdx.x;
-  const SeqDecision d = p.seq[b];
+  const SeqDecision d = uniform_load(p.seq, b);
   if (d.mode == kDrawNone) return;  // fallback: the decide kernel wrote the result
   draw_sequence<T, VW>(p, b, d);
 }
@@ -525,71 +547,105 @@ __global__ __launch_bounds__(kWave) void k_chain_draw(ChainParams p) {
 // ------------------------------------------------------------------------------------ alpha
 
 // Acceptance rate alpha_i = sum_x min(p_i(x), q_i(x)) of position i of sequence b (the Step 3
-// accept probability averaged over x ~ q_i), one workgroup per (b, i).  Waves 0 and 1 merge the
-// chunk partials of target row i and draft row i; then every wave takes chunks c = wave,
-// wave + waves, ... and adds s * sum_x min(ra e_t(x), rb e_d(x)) for the chunk, where e_t, e_d
-// are the chunk-local softmax terms, A and B the chunk scales taking them to p and q,
-// s = max(A, B) and (ra, rb) = (A, B) / s (one of them is 1, the other at most 1, so nothing
-// overflows); the wave sums are added in wave order (deterministic).  The sweep that produced the
-// partials covered rows [target 0..gamma-1, draft 0..gamma-1] of every sequence.
-constexpr int kAlphaBlock = 512;
-constexpr int kAlphaWaves = kAlphaBlock / kWave;
+// accept probability averaged over x ~ q_i).  The sweep that produced the partials covered rows
+// [target 0..gamma-1, draft 0..gamma-1] of every sequence.  Three kernels follow it:
+//   merge    one wave per row merges its chunk partials into (M, S).
+//   overlap  one wave per (b, i, chunk c) adds s * sum_x min(ra e_t(x), rb e_d(x)) over chunk c
+//            of target row i and draft row i, where e_t, e_d are the chunk-local softmax terms,
+//            A and B the chunk scales taking them to p and q, s = max(A, B) and
+//            (ra, rb) = (A, B) / s (one of them is 1, the other at most 1, so nothing
+//            overflows).  A chunk where A or B is 0 adds nothing.  The chunk loads go out first;
+//            the row statistics and chunk partials arrive through the scalar cache meanwhile.
+//            Workgroups are sized like the sweep's (measured: 1024 threads for fp32, 256 for
+//            bf16; a workgroup per (b, i) with waves looping over the chunks ran at 0.47 of
+//            the HBM peak on 131 MB of bf16, this form at 0.68).
+//   reduce   one wave per (b, i) adds the chunk sums in a fixed order (deterministic).
+constexpr int kAlphaBlock = 256;
+
+__global__ __launch_bounds__(kAlphaBlock) void k_chain_alpha_merge(ChainParams p, int64_t rows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t r = int64_t(blockIdx.x) * (kAlphaBlock / kWave) + wave_id();
+  if (r >= rows) return;  // wave-uniform
+  const int64_t b = r / (2 * p.gamma);
+  const double Td = effective_temperature(uniform_load(p.temp, b));
+  const RowStat st = merge_row(p.part + r * p.nchunk, p.nchunk, lane, Td);
+  if (lane == 0) p.rowstat[r] = st;
+}
 
 template <typename T, int VW>
-__global__ __launch_bounds__(kAlphaBlock) void k_chain_alpha(ChainParams p, float* out_alpha,
-                                                            int32_t* out_status) {
-  __shared__ RowStat st[2];
-  __shared__ double wave_acc[kAlphaWaves];
-  const int gamma = p.gamma;
-  const int64_t b = blockIdx.x / gamma;
-  const int i = int(blockIdx.x - b * gamma);
-  const int R = 2 * gamma;
-  const int64_t nchunk = p.nchunk;
-  const int wave = wave_id();
+__global__ __launch_bounds__(kStreamBlock<T>) void k_chain_alpha(ChainParams p, double* chunk_sum,
+                                                                int64_t total) {
   const int lane = threadIdx.x & (kWave - 1);
-  const float tb = p.temp[b];
-  const float te = effective_temperature(tb);
+  const int64_t w = int64_t(blockIdx.x) * (kStreamBlock<T> / kWave) + wave_id();
+  if (w >= total) return;  // wave-uniform
+  const int gamma = p.gamma;
+  const int64_t V = p.V, nchunk = p.nchunk;
+  const int64_t pair = w / nchunk;
+  const int64_t c = w - pair * nchunk;
+  const int64_t b = pair / gamma;
+  const int i = int(pair - b * gamma);
+  const int64_t jt = b * (2 * gamma) + i, jd = jt + gamma;  // rows of the partials
+  const int nvalid = chunk_valid(V, c);
+  RawChunk<T, VW> rt, rd;
+  load_raw<T, VW>(static_cast<const T*>(p.tgt) + (b * (gamma + 1) + i) * V + c * kChunk, nvalid,
+                  lane, rt);
+  load_raw<T, VW>(static_cast<const T*>(p.drf) + (b * gamma + i) * V + c * kChunk, nvalid, lane,
+                  rd);
+  const float te = effective_temperature(uniform_load(p.temp, b));
   const double Td = te;
   const float kk = log2e_over_t(te);
-  const RowPart* pt = p.part + (b * R + i) * nchunk;
-  const RowPart* pd = p.part + (b * R + gamma + i) * nchunk;
-  if (wave < 2) {
-    const RowStat s = merge_row(wave == 0 ? pt : pd, nchunk, lane, Td);
-    if (lane == 0) st[wave] = s;
-  }
-  __syncthreads();
-  const RowStat st_t = st[0], st_d = st[1];
-  const bool valid = st_t.valid && st_d.valid;
-  const T* zt_row = static_cast<const T*>(p.tgt) + (b * (gamma + 1) + i) * p.V;
-  const T* zd_row = static_cast<const T*>(p.drf) + (b * gamma + i) * p.V;
+  const RowStat st_t = uniform_load(p.rowstat, jt), st_d = uniform_load(p.rowstat, jd);
+  const RowPart ct = uniform_load(p.part, jt * nchunk + c);
+  const RowPart cd = uniform_load(p.part, jd * nchunk + c);
   double acc = 0.0;
-  if (valid) {
-    for (int64_t c = wave; c < nchunk; c += kAlphaWaves) {
-      const RowPart ct = pt[c], cd = pd[c];
-      const double A = chunk_scale(ct.m, st_t, Td), Bq = chunk_scale(cd.m, st_d, Td);
-      if (A > 0.0 && Bq > 0.0) {  // wave-uniform; otherwise min(p, q) is 0 on the chunk
-        float zt[kElemsPerLane], zd[kElemsPerLane];
-        load_chunk<T, VW>(zt_row, p.V, c, lane, zt);
-        load_chunk<T, VW>(zd_row, p.V, c, lane, zd);
-        const double sc = fmax(A, Bq);
-        const float ra = float(A / sc), rb = float(Bq / sc);
-        acc += sc * wave_sum(lane_term_sum([&](int e) {
-                 return fminf(ra * softmax_term(zt[e], ct.m, kk),
-                              rb * softmax_term(zd[e], cd.m, kk));
-               }));
-      }
+  if (st_t.valid && st_d.valid) {  // wave-uniform
+    const double A = chunk_scale(ct.m, st_t, Td), Bq = chunk_scale(cd.m, st_d, Td);
+    if (A > 0.0 && Bq > 0.0) {  // wave-uniform; otherwise min(p, q) is 0 on the chunk
+      float zt[kElemsPerLane], zd[kElemsPerLane];
+      unpack_chunk<T, VW>(rt, nvalid, lane, zt);
+      unpack_chunk<T, VW>(rd, nvalid, lane, zd);
+      const double sc = fmax(A, Bq);
+      const float ra = float(A / sc), rb = float(Bq / sc);
+      acc = sc * wave_sum(lane_term_sum([&](int e) {
+              return fminf(ra * softmax_term(zt[e], ct.m, kk), rb * softmax_term(zd[e], cd.m, kk));
+            }));
     }
   }
-  if (lane == 0) wave_acc[wave] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double alpha = 0.0;
-    for (int w = 0; w < kAlphaWaves; ++w) alpha += wave_acc[w];
-    out_alpha[b * gamma + i] = valid ? float(alpha) : NAN;
+  if (lane == 0) chunk_sum[w] = acc;
+}
+
+__global__ __launch_bounds__(kAlphaBlock) void k_chain_alpha_reduce(ChainParams p,
+                                                                   const double* chunk_sum,
+                                                                   int64_t pairs, float* out_alpha,
+                                                                   int32_t* out_status) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t pair = int64_t(blockIdx.x) * (kAlphaBlock / kWave) + wave_id();
+  if (pair >= pairs) return;  // wave-uniform
+  const int gamma = p.gamma;
+  const int64_t nchunk = p.nchunk;
+  const int64_t b = pair / gamma;
+  const int64_t jt = b * (2 * gamma) + (pair - b * gamma), jd = jt + gamma;
+  const double* cs = chunk_sum + pair * nchunk;
+  double acc = 0.0;
+  for (int64_t c0 = 0; c0 < nchunk; c0 += int64_t(kWave) * kMergeBatch) {
+    double v[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int64_t c = c0 + int64_t(k) * kWave + lane;
+      v[k] = c < nchunk ? cs[c] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) acc += v[k];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    const bool valid = uniform_load(p.rowstat, jt).valid && uniform_load(p.rowstat, jd).valid;
+    out_alpha[pair] = valid ? float(acc) : NAN;
     if (out_status) {
+      const float tb = uniform_load(p.temp, b);
       int bits = valid ? 0 : SV_ROW_NONFINITE;
       if (!(tb > 0.0f && tb < INFINITY)) bits |= SV_ROW_BAD_TEMPERATURE;
-      out_status[b * gamma + i] = bits;
+      out_status[pair] = bits;
     }
   }
 }
@@ -606,16 +662,29 @@ hipError_t run_alpha(const AlphaArgs& a, hipStream_t s) {
   p.V = a.V;
   p.nchunk = L.nchunk;
   p.part = reinterpret_cast<RowPart*>(a.ws + L.off_part);
-  const int64_t total = int64_t(a.B) * (2 * a.gamma) * L.nchunk;
+  p.rowstat = reinterpret_cast<RowStat*>(a.ws + L.off_rowstat);
+  double* chunk_sum = reinterpret_cast<double*>(a.ws + L.off_chunk_sum);
+  const int64_t rows = int64_t(a.B) * (2 * a.gamma);
+  const int64_t total = rows * L.nchunk;
   const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
   constexpr int wpb = kStreamBlock<T> / kWave;
   hipError_t e = launch_kernel("alpha_sweep", k_chain_sweep<T, VW>,
                                dim3(unsigned((waves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
                                p, total);
   if (e != hipSuccess) return e;
-  return launch_kernel("alpha_overlap", k_chain_alpha<T, VW>,
-                       dim3(unsigned(int64_t(a.B) * a.gamma)), dim3(kAlphaBlock), s, p,
-                       a.out_alpha, a.out_status);
+  constexpr int awpb = kAlphaBlock / kWave;
+  e = launch_kernel("alpha_merge", k_chain_alpha_merge, dim3(unsigned((rows + awpb - 1) / awpb)),
+                    dim3(kAlphaBlock), s, p, rows);
+  if (e != hipSuccess) return e;
+  const int64_t pairs = int64_t(a.B) * a.gamma;
+  const int64_t owaves = pairs * L.nchunk;
+  e = launch_kernel("alpha_overlap", k_chain_alpha<T, VW>,
+                    dim3(unsigned((owaves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s, p,
+                    chunk_sum, owaves);
+  if (e != hipSuccess) return e;
+  return launch_kernel("alpha_reduce", k_chain_alpha_reduce,
+                       dim3(unsigned((pairs + awpb - 1) / awpb)), dim3(kAlphaBlock), s, p,
+                       chunk_sum, pairs, a.out_alpha, a.out_status);
 }
 
 // ------------------------------------------------------------------------------------ sampler

@@ -273,11 +273,19 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
 }
 
-// Wave-uniform read of read-only data through the scalar data cache (a scalar load, counted
-// apart from the vector loads, so waiting for it never waits for chunk loads in flight).
+// Wave-uniform read of data that no wave of the running kernel writes, through the scalar data
+// cache (a scalar load, counted apart from the vector loads, so waiting for it never waits for
+// chunk loads in flight).  Records of 16 bytes (the workspace's partials, statistics and
+// decisions) are read as four dwords and reinterpreted.
 template <typename T>
 __device__ __forceinline__ T uniform_load(const T* p, int64_t i) {
-  return ((const __attribute__((address_space(4))) T*)p)[i];
+  if constexpr (sizeof(T) == 16) {
+    static_assert(alignof(T) == 16, "16-byte records must be 16-byte aligned");
+    const u32x4_t v = ((const __attribute__((address_space(4))) u32x4_t*)p)[i];
+    return __builtin_bit_cast(T, v);
+  } else {
+    return ((const __attribute__((address_space(4))) T*)p)[i];
+  }
 }
 
 // 2^x on the hardware transcendental unit (v_exp_f32).

@@ -41,7 +41,7 @@ struct __attribute__((aligned(16))) RowStat {
 // How a finished sequence draws its last token.
 enum DrawMode : int32_t { kDrawNone = 0, kDrawBonus = 1, kDrawResidual = 2 };
 
-// Per sequence decision taken by the sweep kernel for the draw kernel.
+// Per sequence decision taken by the decide kernel for the residual and draw kernels.
 struct __attribute__((aligned(16))) SeqDecision {
   int32_t k;       // drafts accepted
   int32_t mode;    // DrawMode
@@ -119,16 +119,26 @@ inline GreedyLayout greedy_layout(int64_t B, int64_t gamma, int64_t V) {
 
 // Workspace of the acceptance-rate path: per (row, chunk) softmax partials of target rows
 // 0..gamma-1 and draft rows 0..gamma-1 of every sequence.
+// Workspace of the acceptance rates: per (row, chunk) softmax partials of target rows
+// 0..gamma-1 and draft rows 0..gamma-1, the merged statistics of those rows, and per
+// (sequence, position, chunk) overlap sums.
 struct AlphaLayout {
   int64_t nchunk;
-  size_t off_part, total;
+  size_t off_part, off_rowstat, off_chunk_sum, total;
 };
 
 inline AlphaLayout alpha_layout(int64_t B, int64_t gamma, int64_t V) {
   AlphaLayout L;
   L.nchunk = n_chunks(V);
-  L.off_part = 0;
-  L.total = align256(sizeof(RowPart) * size_t(B) * size_t(2 * gamma) * size_t(L.nchunk));
+  const size_t rows = size_t(B) * size_t(2 * gamma);
+  size_t off = 0;
+  L.off_part = off;
+  off += align256(sizeof(RowPart) * rows * size_t(L.nchunk));
+  L.off_rowstat = off;
+  off += align256(sizeof(RowStat) * rows);
+  L.off_chunk_sum = off;
+  off += align256(sizeof(double) * size_t(B) * size_t(gamma) * size_t(L.nchunk));
+  L.total = off;
   return L;
 }
 

@@ -2,6 +2,7 @@
 // types, returning the launch status directly, and optional per-kernel event timing.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <tuple>
@@ -9,11 +10,11 @@
 
 namespace sv {
 
-// Kernel timing (see sv_trace_* in the C ABI).  When tracing is on, trace_before/trace_after
-// record a HIP event on the launch stream immediately before and after the kernel.
+// Kernel timing (see sv_trace_* in the C ABI).  When tracing is on, trace_slot hands out the
+// next pair of events and the kernel is launched with hipExtLaunchKernel, which stamps them
+// with the start and end time of the kernel's own execution (no gap before or after it).
 bool trace_on();
-void trace_before(const char* name, hipStream_t stream);
-void trace_after(hipStream_t stream);
+bool trace_slot(const char* name, hipEvent_t* begin, hipEvent_t* end);
 
 template <typename... KArgs, typename... Args>
 hipError_t launch_kernel_shm(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block,
@@ -27,13 +28,12 @@ hipError_t launch_kernel_shm(const char* name, void (*kernel)(KArgs...), dim3 gr
         ((ptrs[i++] = static_cast<void*>(&e)), ...);
       },
       held);
-  const bool tr = trace_on();
-  if (tr) trace_before(name, stream);
-  const hipError_t err =
-      hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shared_bytes,
-                      stream);
-  if (tr) trace_after(stream);
-  return err;
+  hipEvent_t t0 = nullptr, t1 = nullptr;
+  if (trace_on() && trace_slot(name, &t0, &t1))
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs,
+                              shared_bytes, stream, t0, t1, 0);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shared_bytes,
+                         stream);
 }
 
 template <typename... KArgs, typename... Args>

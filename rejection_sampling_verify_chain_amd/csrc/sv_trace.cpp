@@ -1,10 +1,11 @@
 // Optional per-kernel GPU timing with HIP events (benchmark support).
 //
 // sv_trace_start(capacity) pre-creates 2*capacity events; each later kernel launch made by
-// the library (up to `capacity` launches) is bracketed by two events recorded on its launch
-// stream.  sv_trace_stop() ends recording; sv_trace_kernels()/sv_trace_get() wait for the
-// recorded events and report, per kernel name, the launch count and total and minimum
-// event-to-event time.  Only host memory and HIP event objects are allocated.
+// the library (up to `capacity` launches) is given two of them, which the launch stamps with
+// the start and end time of that kernel's execution on its stream.  sv_trace_stop() ends
+// recording; sv_trace_kernels()/sv_trace_get() wait for the recorded events and report, per
+// kernel name, the launch count and total and minimum event-to-event time.  Only host memory
+// and HIP event objects are allocated.
 
 #include <string.h>
 
@@ -52,19 +53,14 @@ namespace sv {
 
 bool trace_on() { return g_on.load(std::memory_order_relaxed); }
 
-void trace_before(const char* name, hipStream_t stream) {
+bool trace_slot(const char* name, hipEvent_t* begin, hipEvent_t* end) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on || g_used >= g_slots.size()) return;
-  Slot& s = g_slots[g_used];
+  if (!g_on || g_used >= g_slots.size()) return false;
+  Slot& s = g_slots[g_used++];
   s.name = name;
-  (void)hipEventRecord(s.begin, stream);
-}
-
-void trace_after(hipStream_t stream) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on || g_used >= g_slots.size()) return;
-  (void)hipEventRecord(g_slots[g_used].end, stream);
-  ++g_used;
+  *begin = s.begin;
+  *end = s.end;
+  return true;
 }
 
 }  // namespace sv

@@ -10,11 +10,12 @@
 //   argmax  the single HBM sweep (launch_argmax_rows): each wave owns one chunk (2048
 //           elements) of one node's logit row and writes the chunk maximum over non-NaN entries
 //           and the lowest index attaining it.
-//   walk    one workgroup per tree merges the partials into g[u] for every node (one wave per
-//           node, all partial loads in flight together), validates the parent array, and walks
-//           from the root with one wave: at node u a ballot over the nodes finds the lowest-id
-//           child c with parent u and token g[u]; it writes the accepted path and tokens, then
-//           g of the last accepted node as the bonus token.
+//   walk    one workgroup per tree merges the partials into g[u] for every node, validates
+//           the parent array, and builds a child table in LDS: next[u] = the lowest-id child c
+//           with parent u and token g[u] (an LDS atomic minimum over the nodes).  Following
+//           next[] from the root gives the accepted path; g of its last node is the bonus token.
+//           All global loads of the tree (partials, parents, tokens) are issued together, so
+//           the walk takes one memory round trip before its stores.
 
 #include <math.h>
 
@@ -26,7 +27,10 @@
 namespace sv {
 namespace {
 
-constexpr int kWalkBlock = 1024;  // walk: one wave per node during the merge
+constexpr int kWalkBlock = 1024;
+constexpr int kWalkWaves = kWalkBlock / kWave;
+constexpr int kNodesPerThread = kMaxTreeNodes / kWalkBlock;
+static_assert(kMaxTreeNodes % kWalkBlock == 0, "walk threads cover the largest tree evenly");
 
 struct TreeParams {
   const void* logits;
@@ -43,70 +47,124 @@ struct TreeParams {
   int32_t* out_status;
 };
 
-// Walk state in LDS, sized by the launch to 3 * n_nodes words: argmax, parent and token of
-// every node.  Only the walk workgroup of a tree uses it.
+// Walk state in LDS: argmax, token and matching child of every node (the launch sizes the
+// dynamic LDS to 3 * n_nodes words), and the tree's status bits.
 struct WalkShared {
   int32_t* g;
-  int32_t* par;
   int32_t* tok;
-  int32_t flags;
+  int32_t* next;
+  int32_t* flags;
 };
 
+// Lanes per node in the partials' merge: the smallest power of two holding the row's chunks,
+// at most a wave; a wave merges kWave / G nodes at once.
+__device__ __forceinline__ int merge_group(int64_t nchunk) {
+  int g = 1;
+  while (g < kWave && g < nchunk) g <<= 1;
+  return g;
+}
+
 // Completes tree t from its chunk partials (all threads of the workgroup).
-__device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
+__device__ void finish_tree(const TreeParams& p, int64_t t, const WalkShared& sh) {
   const int n_nodes = p.n_nodes;
   const int64_t base = t * n_nodes;
   const int64_t nchunk = p.nchunk;
   const int wave = wave_id();
   const int lane = threadIdx.x & (kWave - 1);
-  if (threadIdx.x == 0) sh.flags = 0;
-  __syncthreads();
+
+  // Parent and token of this thread's nodes u = threadIdx.x + q * kWalkBlock.
+  int32_t par[kNodesPerThread], tok[kNodesPerThread];
+#pragma unroll
+  for (int q = 0; q < kNodesPerThread; ++q) {
+    const int u = int(threadIdx.x) + q * kWalkBlock;
+    par[q] = u < n_nodes ? p.parents[base + u] : 0;
+    tok[q] = u < n_nodes ? p.node_tokens[base + u] : 0;
+  }
+
+  // g[u] for every node: G lanes per node, each lane taking chunks sub, sub + G, ...,
+  // kMergeBatch loads in flight per lane, then a reduction inside the G-lane group.
+  const int G = merge_group(nchunk);
+  const int per_wave = kWave / G;
+  const int sub = lane & (G - 1);
   int local = 0;
-  for (int u = wave; u < n_nodes; u += kWalkBlock / kWave) {
-    int32_t gu;
-    int nan;
-    merge_row_argmax(p.part + (base + u) * nchunk, nchunk, lane, &gu, &nan);
-    if (lane == 0) {
+  for (int u0 = wave * per_wave; u0 < n_nodes; u0 += kWalkWaves * per_wave) {
+    const int u = u0 + lane / G;
+    float best = -INFINITY;
+    int32_t bidx = INT32_MAX;
+    int anynan = 0;
+    if (u < n_nodes) {
+      const ArgPart* pp = p.part + (base + u) * nchunk;
+      for (int64_t c0 = sub; c0 < nchunk; c0 += int64_t(G) * kMergeBatch) {
+        ArgPart r[kMergeBatch];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+          const int64_t c = c0 + int64_t(i) * G;
+          r[i] = c < nchunk ? pp[c] : ArgPart{-INFINITY, INT32_MAX, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+          if (arg_better(r[i].v, r[i].idx, best, bidx)) {
+            best = r[i].v;
+            bidx = r[i].idx;
+          }
+          anynan |= r[i].nan;
+        }
+      }
+    }
+    for (int o = G / 2; o > 0; o >>= 1) {  // xor offsets below G stay inside the group
+      const float ov = __shfl_xor(best, o, kWave);
+      const int32_t oi = __shfl_xor(bidx, o, kWave);
+      anynan |= __shfl_xor(anynan, o, kWave);
+      if (arg_better(ov, oi, best, bidx)) {
+        best = ov;
+        bidx = oi;
+      }
+    }
+    if (sub == 0 && u < n_nodes) {
+      const int32_t gu = bidx == INT32_MAX ? 0 : bidx;
       sh.g[u] = gu;
       if (p.out_g) p.out_g[base + u] = gu;
-      if (nan) local |= SV_ROW_NONFINITE;
+      if (anynan) local |= SV_ROW_NONFINITE;
     }
   }
-  for (int u = threadIdx.x; u < n_nodes; u += kWalkBlock) {
-    const int32_t pu = p.parents[base + u];
-    const int32_t tu = p.node_tokens[base + u];
-    sh.par[u] = pu;
-    sh.tok[u] = tu;
-    if (u == 0 ? pu != -1 : (pu < 0 || pu >= u)) local |= SV_ROW_BAD_TREE;
-    if (u > 0 && (tu < 0 || int64_t(tu) >= p.V)) local |= SV_ROW_TOKEN_RANGE;
+
+#pragma unroll
+  for (int q = 0; q < kNodesPerThread; ++q) {
+    const int u = int(threadIdx.x) + q * kWalkBlock;
+    if (u < n_nodes) {
+      sh.tok[u] = tok[q];
+      sh.next[u] = INT32_MAX;
+      if (u == 0 ? par[q] != -1 : (par[q] < 0 || par[q] >= u)) local |= SV_ROW_BAD_TREE;
+      if (u > 0 && (tok[q] < 0 || int64_t(tok[q]) >= p.V)) local |= SV_ROW_TOKEN_RANGE;
+    }
   }
-  if (local) atomicOr(&sh.flags, local);
+  if (threadIdx.x == 0) *sh.flags = 0;
+  __syncthreads();
+
+  // next[u] = lowest-id child of u whose token is g[u] (edges that break the parent order are
+  // left out; a tree holding one is not walked).
+  if (local) atomicOr(sh.flags, local);
+#pragma unroll
+  for (int q = 0; q < kNodesPerThread; ++q) {
+    const int u = int(threadIdx.x) + q * kWalkBlock;
+    if (u > 0 && u < n_nodes && par[q] >= 0 && par[q] < u && tok[q] == sh.g[par[q]])
+      atomicMin(&sh.next[par[q]], u);
+  }
   __syncthreads();
   if (threadIdx.x >= kWave) return;
-  const int status = sh.flags;
+  const int status = *sh.flags;
 
   int k = 0;
   int u = 0;
   if (!(status & (SV_ROW_BAD_TREE | SV_ROW_TOKEN_RANGE))) {
-    for (;;) {
-      const int32_t want = sh.g[u];
-      int found = -1;
-      for (int b0 = 0; b0 < n_nodes; b0 += kWave) {
-        const int i = b0 + lane;
-        const bool m = i > 0 && i < n_nodes && sh.par[i] == u && sh.tok[i] == want;
-        const uint64_t hit = __ballot(m);
-        if (hit) {
-          found = b0 + __builtin_ctzll(hit);
-          break;
-        }
-      }
-      if (found < 0) break;  // parents precede children, so the walk ends within n_nodes steps
+    // Children have larger ids than their parents, so the walk ends within n_nodes steps.
+    for (int c = sh.next[0]; c != INT32_MAX; c = sh.next[c]) {
       ++k;
       if (lane == 0) {
-        p.out_path[base + k] = found;
-        p.out_tokens[base + k - 1] = sh.tok[found];
+        p.out_path[base + k] = c;
+        p.out_tokens[base + k - 1] = sh.tok[c];
       }
-      u = found;
+      u = c;
     }
   }
   for (int i = lane; i < n_nodes; i += kWave) {
@@ -123,12 +181,8 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, WalkShared& sh) {
 
 __global__ __launch_bounds__(kWalkBlock) void k_tree_walk(TreeParams p) {
   extern __shared__ int32_t walk_lds[];
-  __shared__ WalkShared sh;
-  if (threadIdx.x == 0) {
-    sh.g = walk_lds;
-    sh.par = walk_lds + p.n_nodes;
-    sh.tok = walk_lds + 2 * p.n_nodes;
-  }
+  __shared__ int32_t flags;
+  WalkShared sh{walk_lds, walk_lds + p.n_nodes, walk_lds + 2 * p.n_nodes, &flags};
   finish_tree(p, blockIdx.x, sh);
 }
 
