@@ -229,30 +229,68 @@ __device__ __forceinline__ void stream_wave(int64_t gw, int64_t total, int64_t n
 }
 
 // ---------------------------------------------------------------------------- wave collectives
-// Butterfly (xor) reductions: every lane ends with the same, bitwise identical value.
+// All-lane reductions over a full wave (all 64 lanes active).  Inside each row of 16 lanes four
+// DPP steps combine partners (quad swaps, then the half-row and row mirrors), leaving the row's
+// result in all 16 lanes; the four row results are read out with readlane and combined in one
+// fixed order.  Every lane ends with the same, bitwise identical value (each DPP step combines
+// two equal-shaped halves, and the operations are commutative).  DPP runs in the vector ALU;
+// the cross-lane shuffle it replaces goes through the LDS crossbar once per step.
+
+// dpp_ctrl values: quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.
+constexpr int kDppQuadSwap1 = 0xB1;
+constexpr int kDppQuadSwap2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = uint32_t(dpp<CTRL>(int(uint32_t(u)))), hi = uint32_t(dpp<CTRL>(int(uint32_t(u >> 32))));
+  return __longlong_as_double((uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ int lane_read(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_read(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double lane_read(double v, int l) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), l));
+  return __longlong_as_double((uint64_t(hi) << 32) | lo);
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce(T v, Op op) {
+  v = op(v, dpp<kDppQuadSwap1>(v));
+  v = op(v, dpp<kDppQuadSwap2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  v = op(v, dpp<kDppMirror>(v));
+  return op(op(lane_read(v, 0), lane_read(v, 16)), op(lane_read(v, 32), lane_read(v, 48)));
+}
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_allreduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_allreduce(v, [](double a, double b) { return a + b; });
 }
 
 __device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_allreduce(v, [](int a, int b) { return min(a, b); });
 }
 
 __device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_allreduce(v, [](int a, int b) { return max(a, b); });
 }
 
 // Inclusive prefix sum over the lanes of a wave (Hillis-Steele).
