@@ -104,6 +104,10 @@ const char* sv_status_string(sv_status status);
  * out_q are unspecified.
  * Any base pointer alignment is accepted; 16-byte-aligned logits with V a multiple of 4 (fp32)
  * or 8 (bf16) take the vector-load path.
+ * Execution: up to 256 sequences of at most 256 KiB of logits each (vector-load path) run in a
+ * single launch, one workgroup per sequence; larger problems take four launches.  Both give
+ * bit-identical results.  The environment variable SPECVERIFY_CHAIN_PATH=fused or =split, read
+ * on every call, forces one of them (testing and measurement).
  * ---------------------------------------------------------------------------------------- */
 size_t sv_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int64_t V, sv_dtype dtype);
 

@@ -8,7 +8,9 @@
 // norm(max(0, p - q)), and the expected-speedup section the (gamma+1)-th token
 // of a fully accepted round.
 //
-// Four launches per call, all on the caller's stream, no host synchronisation:
+// Sequences with small rows (up to 256 KiB of logits, at most 256 sequences) take a single
+// launch, chain_fused, one workgroup per sequence (its section below).  Otherwise four
+// launches per call, all on the caller's stream, no host synchronisation:
 //   sweep     the single HBM sweep over all B*(2*gamma+1)*V logits: each wave owns one chunk
 //             (2048 elements) of one logit row and writes its chunk max m_c and
 //             S_c = sum exp((z - m_c)/T) (fp32 terms, fp64 sum).
@@ -27,6 +29,8 @@
 // XCD lags.
 
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -219,45 +223,38 @@ struct DecideShared {
   RowStat st[2 * kMaxGamma + 1];
 };
 
-// The decision for sequence b from the chunk partials of its rows.  Called by all threads of
-// the sequence's workgroup.  Wave 0 first fetches the draft tokens and gathers the two logits
-// each one picks, so that those dependent loads overlap the partials' merge.
-template <typename T, int VW>
-__device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& sh) {
-  const T* tgt = static_cast<const T*>(p.tgt);
-  const T* drf = static_cast<const T*>(p.drf);
+// The drafted token of position `lane` (lanes < gamma of one wave) and the target and draft
+// logits it picks, fetched ahead of the decision.
+struct Drafted {
+  int x;
+  bool bad;  // x outside [0, V)
+  float zt, zd;
+};
+
+template <typename T>
+__device__ __forceinline__ Drafted gather_drafted(const ChainParams& p, int64_t b, int lane) {
+  Drafted g{0, false, 0.0f, 0.0f};
+  if (lane < p.gamma) {
+    const T* tgt = static_cast<const T*>(p.tgt);
+    const T* drf = static_cast<const T*>(p.drf);
+    g.x = p.toks[b * p.gamma + lane];
+    g.bad = (g.x < 0) || (int64_t(g.x) >= p.V);
+    if (!g.bad) {
+      g.zt = widen(chain_row(tgt, drf, b, p.gamma, lane, p.V)[g.x]);
+      g.zd = widen(chain_row(tgt, drf, b, p.gamma, p.gamma + 1 + lane, p.V)[g.x]);
+    }
+  }
+  return g;
+}
+
+// The decision of sequence b from its row statistics st[0 .. 2*gamma] (one wave, lane i =
+// position i): input checks, p_i(x_i) and q_i(x_i) in fp64, the accept bits and the cut.
+// Writes p, q, the accepted prefix with its padding, and the fallback result; returns the
+// decision (the same on every lane).
+__device__ SeqDecision decide_from_stats(const ChainParams& p, int64_t b, const RowStat* st,
+                                         const Drafted& g, float tb, double Td, int lane) {
   const int gamma = p.gamma;
-  const int64_t V = p.V, nchunk = p.nchunk;
   const int R = 2 * gamma + 1;
-  const int wave = wave_id();
-  const int lane = threadIdx.x & (kWave - 1);
-  const float tb = uniform_load(p.temp, b);
-  const double Td = effective_temperature(tb);
-
-  int x = 0;
-  bool xbad = false;
-  float zt_x = 0.0f, zd_x = 0.0f;
-  if (wave == 0 && lane < gamma) {
-    x = p.toks[b * gamma + lane];
-    xbad = (x < 0) || (int64_t(x) >= V);
-    if (!xbad) {
-      zt_x = widen(chain_row(tgt, drf, b, gamma, lane, V)[x]);
-      zd_x = widen(chain_row(tgt, drf, b, gamma, gamma + 1 + lane, V)[x]);
-    }
-  }
-
-  // Row max and normaliser of every row of the sequence, one wave per row.
-  for (int j = wave; j < R; j += kWavesPerBlock) {
-    const RowStat st = merge_row(p.part + (b * R + j) * nchunk, nchunk, lane, Td);
-    if (lane == 0) {
-      sh.st[j] = st;
-      p.rowstat[b * R + j] = st;
-    }
-  }
-  __syncthreads();
-  if (wave != 0) return;
-
-  // Accept tests (lane i = position i) and the cut.
   int status = 0;
   if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
   bool bad = false;
@@ -266,9 +263,9 @@ __device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& s
     bad |= !(u >= 0.0f && u < 1.0f);
   }
   if (__any(bad)) status |= SV_ROW_BAD_UNIFORM;
-  if (__any(xbad)) status |= SV_ROW_TOKEN_RANGE;
+  if (__any(g.bad)) status |= SV_ROW_TOKEN_RANGE;
   bad = false;
-  for (int j = lane; j < R; j += kWave) bad |= !sh.st[j].valid;
+  for (int j = lane; j < R; j += kWave) bad |= !st[j].valid;
   if (__any(bad)) status |= SV_ROW_NONFINITE;
 
   const bool fallback = (status & (SV_ROW_TOKEN_RANGE | SV_ROW_NONFINITE |
@@ -277,10 +274,10 @@ __device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& s
   if (!fallback) {
     bool accept = false;
     if (lane < gamma) {
-      const RowStat a = sh.st[lane];
-      const RowStat d = sh.st[gamma + 1 + lane];
-      const double pi = exp((double(zt_x) - double(a.m)) / Td) / a.s;
-      const double qi = exp((double(zd_x) - double(d.m)) / Td) / d.s;
+      const RowStat a = st[lane];
+      const RowStat d = st[gamma + 1 + lane];
+      const double pi = exp((double(g.zt) - double(a.m)) / Td) / a.s;
+      const double qi = exp((double(g.zd) - double(d.m)) / Td) / d.s;
       const double u = p.uni[b * (gamma + 1) + lane];
       if (qi > 0.0) {
         accept = u < fmin(1.0, pi / qi);
@@ -298,21 +295,46 @@ __device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& s
     if (p.out_p) p.out_p[b * gamma + lane] = NAN;
     if (p.out_q) p.out_q[b * gamma + lane] = NAN;
   }
-  // Accepted prefix and padding; position k is written by the draw kernel.
+  // Accepted prefix and padding; position k is written by the draw.
   for (int i = lane; i <= gamma; i += kWave) {
     int32_t v = -1;
-    if (i < k) v = x;  // i < k <= gamma <= 64 only on the first pass, where lane i holds x_i
+    if (i < k) v = g.x;  // i < k <= gamma <= 64 only on the first pass, where lane i holds x_i
     if (fallback && i == 0) v = 0;
     p.out_tokens[b * (gamma + 1) + i] = v;
   }
-  if (lane == 0) {
-    p.seq[b] = SeqDecision{k, fallback ? kDrawNone : (k < gamma ? kDrawResidual : kDrawBonus),
-                           status, 0};
-    if (fallback) {
-      p.out_nacc[b] = 0;
-      if (p.out_status) p.out_status[b] = status;
+  if (fallback && lane == 0) {
+    p.out_nacc[b] = 0;
+    if (p.out_status) p.out_status[b] = status;
+  }
+  return SeqDecision{k, fallback ? kDrawNone : (k < gamma ? kDrawResidual : kDrawBonus), status,
+                     0};
+}
+
+// The decision for sequence b from the chunk partials of its rows (all threads of the
+// sequence's workgroup).  Wave 0 first fetches the drafted tokens' logits, so that those
+// dependent loads overlap the partials' merge.
+template <typename T, int VW>
+__device__ void decide_sequence(const ChainParams& p, int64_t b, DecideShared& sh) {
+  const int R = 2 * p.gamma + 1;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & (kWave - 1);
+  const float tb = uniform_load(p.temp, b);
+  const double Td = effective_temperature(tb);
+  Drafted g{0, false, 0.0f, 0.0f};
+  if (wave == 0) g = gather_drafted<T>(p, b, lane);
+
+  // Row max and normaliser of every row of the sequence, one wave per row.
+  for (int j = wave; j < R; j += kWavesPerBlock) {
+    const RowStat st = merge_row(p.part + (b * R + j) * p.nchunk, p.nchunk, lane, Td);
+    if (lane == 0) {
+      sh.st[j] = st;
+      p.rowstat[b * R + j] = st;
     }
   }
+  __syncthreads();
+  if (wave != 0) return;
+  const SeqDecision d = decide_from_stats(p, b, sh.st, g, tb, Td, lane);
+  if (lane == 0) p.seq[b] = d;
 }
 
 // Inverse-CDF step over chunk masses (one wave): total W of the masses in chunk order, then
@@ -392,18 +414,44 @@ __device__ Located locate_chunk(int64_t nchunk, int lane, double u, MassFn mass)
   return Located{last_c < 0 ? 0 : last_c, last_before, total};
 }
 
+// Where the draw finds a sequence's row statistics, chunk partials and residual masses.
+// WorkspaceSrc reads the workspace written by earlier kernels: wave-uniform records through the
+// scalar cache (issued beside the vector loads they do not depend on), the per-lane chunk masses
+// with vector loads.  LdsSrc reads the copies that the one-workgroup path keeps in LDS.
+struct WorkspaceSrc {
+  const ChainParams& p;
+  int64_t b;
+  __device__ RowStat stat(int j) const { return uniform_load(p.rowstat, b * (2 * p.gamma + 1) + j); }
+  __device__ RowPart part(int j, int64_t c) const {
+    return uniform_load(p.part, (b * (2 * p.gamma + 1) + j) * p.nchunk + c);
+  }
+  __device__ RowPart part_lane(int j, int64_t c) const {
+    return p.part[(b * (2 * p.gamma + 1) + j) * p.nchunk + c];
+  }
+  __device__ double wres(int64_t c) const { return p.wres[b * p.nchunk + c]; }
+};
+
+struct LdsSrc {
+  const RowStat* st;   // [2 * gamma + 1]
+  const RowPart* prt;  // [2 * gamma + 1][nchunk]
+  const double* wr;    // [nchunk]
+  int64_t nchunk;
+  __device__ RowStat stat(int j) const { return st[j]; }
+  __device__ RowPart part(int j, int64_t c) const { return prt[j * nchunk + c]; }
+  __device__ RowPart part_lane(int j, int64_t c) const { return prt[j * nchunk + c]; }
+  __device__ double wres(int64_t c) const { return wr[c]; }
+};
+
 // Draw of sequence b (one wave): residual draw over the residual chunk masses (falling back to
-// p_k if they sum to zero), or the bonus draw from p_gamma over the sweep's chunk masses.  The
-// wave-uniform records (row statistics, the located chunk's partials, T, u) come through the
-// scalar cache, issued beside the vector loads they do not depend on, so the draw takes three
-// dependent memory round trips: the decision, the chunk masses, the located chunk.
-template <typename T, int VW>
-__device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision& d) {
+// p_k if they sum to zero), or the bonus draw from p_gamma over the sweep's chunk masses.  It
+// takes three dependent memory round trips: the decision, the chunk masses, the located chunk.
+template <typename T, int VW, typename Src>
+__device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision& d,
+                              const Src& src) {
   const T* tgt = static_cast<const T*>(p.tgt);
   const T* drf = static_cast<const T*>(p.drf);
   const int gamma = p.gamma;
   const int64_t V = p.V, nchunk = p.nchunk;
-  const int R = 2 * gamma + 1;
   const int lane = threadIdx.x & (kWave - 1);
   const float te = effective_temperature(uniform_load(p.temp, b));
   const double Td = te;
@@ -415,18 +463,17 @@ __device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision
   int64_t y = -1;
   if (d.mode == kDrawResidual) {
     const int jt = k, jd = gamma + 1 + k;
-    const RowStat st_t = uniform_load(p.rowstat, b * R + jt);
-    const RowStat st_d = uniform_load(p.rowstat, b * R + jd);
-    const double* wr = p.wres + b * nchunk;
-    const Located at = locate_chunk(nchunk, lane, u, [&](int64_t c) { return wr[c]; });
+    const RowStat st_t = src.stat(jt);
+    const RowStat st_d = src.stat(jd);
+    const Located at = locate_chunk(nchunk, lane, u, [&](int64_t c) { return src.wres(c); });
     if (at.total > 0.0) {
       const int64_t cs = at.chunk;
       const int nvalid = chunk_valid(V, cs);
       RawChunk<T, VW> rt, rd;
       load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jt, V) + cs * kChunk, nvalid, lane, rt);
       load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jd, V) + cs * kChunk, nvalid, lane, rd);
-      const RowPart pt = uniform_load(p.part, (b * R + jt) * nchunk + cs);
-      const RowPart pd = uniform_load(p.part, (b * R + jd) * nchunk + cs);
+      const RowPart pt = src.part(jt, cs);
+      const RowPart pd = src.part(jd, cs);
       const ResidualScale rs =
           residual_scale(chunk_scale(pt.m, st_t, Td), chunk_scale(pd.m, st_d, Td));
       float zt[kElemsPerLane], zd[kElemsPerLane];
@@ -443,17 +490,16 @@ __device__ void draw_sequence(const ChainParams& p, int64_t b, const SeqDecision
   if (y < 0) {
     // Bonus draw from p_gamma, or the zero-residual fallback from p_k.
     const int jr = d.mode == kDrawBonus ? gamma : k;
-    const RowStat srow = uniform_load(p.rowstat, b * R + jr);
-    const RowPart* pp = p.part + (b * R + jr) * nchunk;
+    const RowStat srow = src.stat(jr);
     const Located at = locate_chunk(nchunk, lane, u, [&](int64_t c) {
-      const RowPart q = pp[c];
+      const RowPart q = src.part_lane(jr, c);
       return q.s * chunk_scale(q.m, srow, Td);
     });
     const int64_t cs = at.chunk;
     const int nvalid = chunk_valid(V, cs);
     RawChunk<T, VW> r;
     load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jr, V) + cs * kChunk, nvalid, lane, r);
-    const RowPart pc = uniform_load(pp, cs);
+    const RowPart pc = src.part(jr, cs);
     const double scale = chunk_scale(pc.m, srow, Td);
     float z[kElemsPerLane];
     unpack_chunk<T, VW>(r, nvalid, lane, z);
@@ -500,6 +546,23 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(ChainParams p) {
   decide_sequence<T, VW>(p, blockIdx.x, sh);
 }
 
+// Residual mass W_c of one chunk (one wave) from its loaded target and draft chunks, their chunk
+// partials and the rows' statistics.  A chunk whose target part is all -inf (A = 0) has none.
+template <typename T, int VW>
+__device__ __forceinline__ double residual_chunk_mass(const RawChunk<T, VW>& rt,
+                                                      const RawChunk<T, VW>& rd, int nvalid,
+                                                      int lane, const RowPart& pt,
+                                                      const RowPart& pd, const RowStat& st_t,
+                                                      const RowStat& st_d, double Td, float kk) {
+  const ResidualScale rs = residual_scale(chunk_scale(pt.m, st_t, Td), chunk_scale(pd.m, st_d, Td));
+  float zt[kElemsPerLane], zd[kElemsPerLane];
+  unpack_chunk<T, VW>(rt, nvalid, lane, zt);
+  unpack_chunk<T, VW>(rd, nvalid, lane, zd);
+  const double wsum = wave_sum(lane_term_sum(
+      [&](int i) { return residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs); }));
+  return rs.A > 0.0 ? rs.A * wsum : 0.0;
+}
+
 // The wave's chunk loads of both rows are issued as soon as the decision (which row) is known;
 // the chunk partials and row statistics that scale them arrive through the scalar cache while
 // the chunk is in flight.  A chunk whose target part is all -inf (A = 0) is loaded too and adds
@@ -522,18 +585,11 @@ __global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p
   load_raw<T, VW>(chain_row(tgt, drf, b, p.gamma, jt, p.V) + c * kChunk, nvalid, lane, rt);
   load_raw<T, VW>(chain_row(tgt, drf, b, p.gamma, jd, p.V) + c * kChunk, nvalid, lane, rd);
   const float te = effective_temperature(uniform_load(p.temp, b));
-  const double Td = te;
-  const float kk = log2e_over_t(te);
-  const RowPart pt = uniform_load(p.part, (b * R + jt) * p.nchunk + c);
-  const RowPart pd = uniform_load(p.part, (b * R + jd) * p.nchunk + c);
-  const ResidualScale rs = residual_scale(chunk_scale(pt.m, uniform_load(p.rowstat, b * R + jt), Td),
-                                          chunk_scale(pd.m, uniform_load(p.rowstat, b * R + jd), Td));
-  float zt[kElemsPerLane], zd[kElemsPerLane];
-  unpack_chunk<T, VW>(rt, nvalid, lane, zt);
-  unpack_chunk<T, VW>(rd, nvalid, lane, zd);
-  const double wsum = wave_sum(lane_term_sum(
-      [&](int i) { return residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs); }));
-  if (lane == 0) p.wres[w] = rs.A > 0.0 ? rs.A * wsum : 0.0;
+  const double w_c = residual_chunk_mass<T, VW>(
+      rt, rd, nvalid, lane, uniform_load(p.part, (b * R + jt) * p.nchunk + c),
+      uniform_load(p.part, (b * R + jd) * p.nchunk + c), uniform_load(p.rowstat, b * R + jt),
+      uniform_load(p.rowstat, b * R + jd), double(te), log2e_over_t(te));
+  if (lane == 0) p.wres[w] = w_c;
 }
 
 template <typename T, int VW>
@@ -541,7 +597,104 @@ __global__ __launch_bounds__(kWave) void k_chain_draw(ChainParams p) {
   const int64_t b = blockIdx.x;
   const SeqDecision d = uniform_load(p.seq, b);
   if (d.mode == kDrawNone) return;  // fallback: the decide kernel wrote the result
-  draw_sequence<T, VW>(p, b, d);
+  draw_sequence<T, VW>(p, b, d, WorkspaceSrc{p, b});
+}
+
+// ------------------------------------------------------------------------ one workgroup per sequence
+//
+// Sequences with small rows run every step in a single launch: one workgroup per sequence sweeps
+// its 2*gamma+1 rows (a chunk per wave at a time), keeps the chunk partials, row statistics,
+// decision and residual masses in LDS, and separates the steps with workgroup barriers.  Each
+// step calls the same device functions as the multi-kernel path, so both give the same bits.
+constexpr int kFusedBlock = 1024;
+constexpr int kFusedWaves = kFusedBlock / kWave;
+template <typename T>
+constexpr int kFusedUnits = kUnitsPerWave<T>;  // chunks per wave in flight: 8 KiB
+
+struct FusedShared {
+  RowStat st[2 * kMaxGamma + 1];
+  SeqDecision d;
+};
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
+  extern __shared__ __align__(16) unsigned char fused_lds[];  // partials [R][nchunk], masses [nchunk]
+  __shared__ FusedShared sh;
+  const int64_t b = blockIdx.x;
+  const int gamma = p.gamma;
+  const int R = 2 * gamma + 1;
+  const int64_t V = p.V, nchunk = p.nchunk;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & (kWave - 1);
+  RowPart* prt = reinterpret_cast<RowPart*>(fused_lds);
+  double* wr = reinterpret_cast<double*>(fused_lds + sizeof(RowPart) * size_t(R) * size_t(nchunk));
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const float tb = uniform_load(p.temp, b);
+  const float te = effective_temperature(tb);
+  const double Td = te;
+  const float kk = log2e_over_t(te);
+
+  Drafted g{0, false, 0.0f, 0.0f};
+  if (wave == 0) g = gather_drafted<T>(p, b, lane);
+
+  // Sweep: the chunk partials of every row (virtual row j as in chain_row), kFusedUnits
+  // consecutive units per wave with all their loads in flight (8 KiB of logits; more spills at
+  // the 128 registers a 1024-thread workgroup allows); a unit past the end reloads the last one
+  // and is not reduced.  Units fit in int: the LDS budget bounds them.
+  constexpr int U = kFusedUnits<T>;
+  const int units = R * int(nchunk);
+  for (int w0 = wave * U; w0 < units; w0 += kFusedWaves * U) {
+    RawChunk<T, VW> r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = min(w0 + u, units - 1);
+      const int j = w / int(nchunk);
+      const int c = w - j * int(nchunk);
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, j, V) + int64_t(c) * kChunk,
+                      chunk_valid(V, c), lane, r[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = w0 + u;
+      if (w < units) {  // wave-uniform
+        const int c = w - (w / int(nchunk)) * int(nchunk);
+        float z[kElemsPerLane];
+        unpack_chunk<T, VW>(r[u], chunk_valid(V, c), lane, z);
+        const RowPart rp = reduce_chunk(z, kk);
+        if (lane == 0) prt[w] = rp;
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = wave; j < R; j += kFusedWaves) {
+    const RowStat st = merge_row(prt + int64_t(j) * nchunk, nchunk, lane, Td);
+    if (lane == 0) sh.st[j] = st;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const SeqDecision d = decide_from_stats(p, b, sh.st, g, tb, Td, lane);
+    if (lane == 0) sh.d = d;
+  }
+  __syncthreads();
+  const SeqDecision d = sh.d;
+  if (d.mode == kDrawNone) return;  // the whole workgroup: the decision wrote the result
+  if (d.mode == kDrawResidual) {     // the whole workgroup
+    const int jt = d.k, jd = gamma + 1 + d.k;
+    for (int64_t c = wave; c < nchunk; c += kFusedWaves) {
+      const int nvalid = chunk_valid(V, c);
+      RawChunk<T, VW> rt, rd;
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jt, V) + c * kChunk, nvalid, lane, rt);
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jd, V) + c * kChunk, nvalid, lane, rd);
+      const double w_c = residual_chunk_mass<T, VW>(rt, rd, nvalid, lane, prt[jt * nchunk + c],
+                                                    prt[jd * nchunk + c], sh.st[jt], sh.st[jd],
+                                                    Td, kk);
+      if (lane == 0) wr[c] = w_c;
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  draw_sequence<T, VW>(p, b, d, LdsSrc{sh.st, prt, wr, nchunk});
 }
 
 // ------------------------------------------------------------------------------------ alpha
@@ -759,6 +912,30 @@ hipError_t run_sample(const SampleArgs& a, hipStream_t s) {
                        s, p, a.uniforms, a.out_tokens, a.out_prob, a.out_status);
 }
 
+// Path choice for chain verification.  The one-workgroup path replaces four launches with one;
+// a workgroup streams about 128 KiB per memory round trip, so it wins while a sequence's rows
+// take at most two such rounds and the grid fits the chip in one wave of workgroups (measured:
+// B = 1, V = 8000 bf16, gamma = 4: 13.8 vs 20.5 us per call; V = 32000: 26.0 vs 20.7 us;
+// B = 256, V = 8000: 18.4 vs 27.2 us; B = 1024: 64 vs 56 us).  It needs the sequence's partials
+// and residual masses to fit its LDS budget.  SPECVERIFY_CHAIN_PATH=fused or =split forces a
+// path (for tests and measurement; "fused" still requires the LDS fit).
+constexpr size_t kFusedMaxLds = 32 * 1024;
+constexpr int64_t kFusedMaxSeqBytes = 256 * 1024;
+constexpr int kFusedMaxBatch = 256;
+
+inline size_t fused_lds_bytes(int gamma, int64_t nchunk) {
+  return sizeof(RowPart) * size_t(2 * gamma + 1) * size_t(nchunk) + sizeof(double) * size_t(nchunk);
+}
+
+inline bool use_fused(const ChainArgs& a, int64_t nchunk, size_t elem_bytes) {
+  if (fused_lds_bytes(a.gamma, nchunk) > kFusedMaxLds) return false;
+  const char* e = getenv("SPECVERIFY_CHAIN_PATH");
+  if (e && strcmp(e, "fused") == 0) return true;
+  if (e && strcmp(e, "split") == 0) return false;
+  return a.B <= kFusedMaxBatch &&
+         int64_t(2 * a.gamma + 1) * a.V * int64_t(elem_bytes) <= kFusedMaxSeqBytes;
+}
+
 template <typename T, int VW>
 hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   const ChainLayout L = chain_layout(a.B, a.gamma, a.V);
@@ -781,6 +958,12 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   p.out_p = a.out_p;
   p.out_q = a.out_q;
   p.out_status = a.out_status;
+
+  if constexpr (VW > 1) {  // the one-element-load forms would spill; they take the split path
+    if (use_fused(a, L.nchunk, sizeof(T)))
+      return launch_kernel_shm("chain_fused", k_chain_fused<T, VW>, dim3(unsigned(a.B)),
+                               dim3(kFusedBlock), fused_lds_bytes(a.gamma, L.nchunk), s, p);
+  }
 
   const int64_t total = int64_t(a.B) * (2 * a.gamma + 1) * L.nchunk;
   const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
