@@ -15,30 +15,47 @@ namespace {
 
 // One wave, one loaded chunk whose first nvalid elements exist -> (max over non-NaN entries,
 // lowest chunk offset holding it (INT32_MAX if none), whether the chunk holds a NaN).  The
-// offset is relative to the chunk start.  Each lane finds its lowest slot i = j * VW + t holding
-// the maximum (slots increase with the chunk offset inside a lane), then a wave minimum over
-// the offsets gives the chunk's lowest.  Branch-free; a chunk of only -inf finds its first
-// in-range -inf element, a chunk of only NaN none.
+// offset is relative to the chunk start.  Chunk offsets grow with (load j, lane, slot t) in
+// that order, so the lowest offset holding the maximum m is found by ballots instead of a
+// per-element search: the first load whose lane maxima include m, the lowest such lane L, then
+// the first slot of load j in lane L equal to m (one compare per load, one per slot of the
+// found load).  Elements past nvalid are -inf and come after every element in range, so in a
+// row's last chunk a hit at or past nvalid means none in range.  A chunk of only NaN has m =
+// NaN and no hit.
 template <int VW, bool TAIL>
 __device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane], int nvalid,
                                                 int lane) {
-  float m = -INFINITY;
+  constexpr int NLD = kElemsPerLane / VW;
+  float mj[NLD];
   bool nan = false;
 #pragma unroll
-  for (int i = 0; i < kElemsPerLane; ++i) {
-    m = fmaxf(m, z[i]);  // NaN never wins
-    nan |= (z[i] != z[i]);
-  }
-  m = wave_max(m);
-  int slot = kElemsPerLane;
+  for (int j = 0; j < NLD; ++j) {
+    float v = z[j * VW];
 #pragma unroll
-  for (int i = kElemsPerLane - 1; i >= 0; --i) {
-    bool hit = z[i] == m;
-    if (TAIL) hit = hit && chunk_offset<VW>(i / VW, lane, i % VW) < nvalid;
-    slot = hit ? i : slot;
+    for (int t = 1; t < VW; ++t) v = fmaxf(v, z[j * VW + t]);  // NaN never wins
+    mj[j] = v;
   }
-  const int off = slot < kElemsPerLane ? chunk_offset<VW>(slot / VW, lane, slot % VW) : INT32_MAX;
-  return ArgPart{m, wave_min(off), __any(nan) ? 1 : 0, 0};
+#pragma unroll
+  for (int i = 0; i < kElemsPerLane; ++i) nan |= (z[i] != z[i]);
+  float lm = mj[0];
+#pragma unroll
+  for (int j = 1; j < NLD; ++j) lm = fmaxf(lm, mj[j]);
+  const float m = wave_max(lm);
+  int off = INT32_MAX;
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const uint64_t h = __ballot(mj[j] == m);
+    if (off == INT32_MAX && h != 0) {  // wave-uniform; taken for the first such load only
+      const int L = __builtin_ctzll(h);
+      int t_first = VW;
+#pragma unroll
+      for (int t = VW - 1; t >= 0; --t)
+        if ((__ballot(z[j * VW + t] == m) >> L) & 1) t_first = t;
+      off = chunk_offset<VW>(j, L, t_first);
+    }
+  }
+  if (TAIL && off >= nvalid) off = INT32_MAX;
+  return ArgPart{m, off, __any(nan) ? 1 : 0, 0};
 }
 
 template <typename T, int VW>

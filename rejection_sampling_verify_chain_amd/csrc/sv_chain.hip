@@ -27,6 +27,9 @@
 // measured slower: the finisher's registers lower the streaming kernel's occupancy, its
 // latency-bound work stretches under a saturated memory system, and it lands on whichever
 // XCD lags.
+//
+// Further down, the per-position acceptance rates and the draft-side sampler reuse the sweep,
+// the row merge and the draw.
 
 #include <math.h>
 #include <stdlib.h>

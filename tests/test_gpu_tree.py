@@ -73,6 +73,32 @@ def test_unaligned_and_signed_zero():
     check_tree(b, out)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("offset", [0, 3])
+def test_argmax_chunk_edges(dtype, offset):
+    """Per-node argmax on designed rows (V = 2048 + 24, so the last chunk holds 24 elements):
+    signed zeros in both orders, ties spread over loads and lanes, a last chunk holding only
+    NaN and -inf, the maximum at the row's last element; vector-load and one-element paths."""
+    V, n = 2048 + 24, 8
+    b = I.tree_random(40, 1, n, V, dtype)
+    z = np.full((1, n, V), -1.0, dtype=np.float32)
+    z[0, 0, 2050], z[0, 0, 2049] = -0.0, 0.0          # +0 first, in the partial chunk
+    z[0, 1, :] = -5.0
+    z[0, 1, 7], z[0, 1, 3] = 0.0, -0.0                # -0 first, in the first chunk
+    z[0, 2, :] = -np.inf
+    z[0, 2, 2048] = np.nan                            # last chunk: NaN then -inf
+    z[0, 3, 2048:] = np.nan                           # last chunk only NaN
+    z[0, 4, [1500, 600, 1030, 2060, 601]] = 7.0       # ties over loads and lanes
+    z[0, 5, V - 1] = 3.0                              # maximum at the last element
+    z[0, 6, :] = np.nan
+    z[0, 6, 1029] = -np.inf                           # one non-NaN element
+    z[0, 7, :] = -np.inf                              # all -inf
+    b.logits = I.bf16_bits(z) if dtype == "bf16" else z
+    out = run_tree(b, offset=offset)
+    assert list(out["node_argmax"][0]) == [2049, 3, 0, 0, 600, V - 1, 1029, 0]
+    check_tree(b, out)
+
+
 def test_golden_greedy_example():
     g = json.load(open(os.path.join(GOLDEN, "p2_greedy_example.json")))
     t = g["tree"]
