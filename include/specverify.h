@@ -119,6 +119,32 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
                           size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Chain verification with per-position acceptance rates ([SpS] Step 3 and expected speedup:
+ * the accept probability alpha, watched in monitoring).
+ *
+ * Exactly sv_verify_chain (same arguments, same outputs, bit for bit), plus
+ *   out_alpha  fp32 [B, gamma] (required): alpha_i = sum_x min(p_i(x), q_i(x)), the probability
+ *              that draft token i is accepted when drawn from q_i, for every position i < gamma
+ *              (NaN where target row i or draft row i has no softmax).  The values equal those of
+ *              sv_chain_acceptance_rates on the same inputs bit for bit.
+ * The rates reuse the verification's sweep and row statistics, so they cost one more pass over
+ * the gamma target and gamma draft rows.  This call always takes the four-launch path, followed
+ * by two more launches.  workspace: at least sv_verify_chain_with_rates_workspace_bytes(B,
+ * gamma, V, dtype) bytes, 256-byte aligned.  Errors as sv_verify_chain; a NULL out_alpha is
+ * SV_ERR_NULL.
+ * ---------------------------------------------------------------------------------------- */
+size_t sv_verify_chain_with_rates_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
+                                                  sv_dtype dtype);
+
+sv_status sv_verify_chain_with_rates(const void* target_logits, const void* draft_logits,
+                                     sv_dtype dtype, const int32_t* draft_tokens,
+                                     const float* uniforms, const float* temperature, int32_t B,
+                                     int32_t gamma, int64_t V, int32_t* out_tokens,
+                                     int32_t* out_num_accepted, float* out_p, float* out_q,
+                                     int32_t* out_status, float* out_alpha, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Greedy token-tree verification ([SpI] basic idea, inference).
  *
  * For each tree t: g[u] = argmax_x logits[t, u, x] for every node u (lowest x on ties, -0 == +0,

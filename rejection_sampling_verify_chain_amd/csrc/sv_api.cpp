@@ -70,25 +70,20 @@ SV_EXPORT const char* sv_status_string(sv_status status) {
   return "unknown sv_status";
 }
 
-SV_EXPORT size_t sv_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
-                                                 sv_dtype dtype) {
-  if (!valid_dtype(dtype) || !chain_shape_ok(B, gamma, V)) return 0;
-  return sv::chain_layout(B, gamma, V).total;
-}
+namespace {
 
-SV_EXPORT sv_status sv_verify_chain(const void* target_logits, const void* draft_logits,
-                                    sv_dtype dtype, const int32_t* draft_tokens,
-                                    const float* uniforms, const float* temperature, int32_t B,
-                                    int32_t gamma, int64_t V, int32_t* out_tokens,
-                                    int32_t* out_num_accepted, float* out_p, float* out_q,
-                                    int32_t* out_status, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+sv_status verify_chain(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                       const int32_t* draft_tokens, const float* uniforms,
+                       const float* temperature, int32_t B, int32_t gamma, int64_t V,
+                       int32_t* out_tokens, int32_t* out_num_accepted, float* out_p, float* out_q,
+                       int32_t* out_status, float* out_alpha, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
   if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !temperature ||
       !out_tokens || !out_num_accepted)
     return SV_ERR_NULL;
   if (!valid_dtype(dtype)) return SV_ERR_DTYPE;
   if (!chain_shape_ok(B, gamma, V)) return SV_ERR_SHAPE;
-  const size_t need = sv::chain_layout(B, gamma, V).total;
+  const size_t need = sv::chain_layout(B, gamma, V, out_alpha != nullptr).total;
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return SV_ERR_WORKSPACE;
 
@@ -107,9 +102,48 @@ SV_EXPORT sv_status sv_verify_chain(const void* target_logits, const void* draft
   a.out_p = out_p;
   a.out_q = out_q;
   a.out_status = out_status;
+  a.out_alpha = out_alpha;
   a.ws = static_cast<char*>(workspace);
   a.vec = aligned16(target_logits) && aligned16(draft_logits) && V % vec_width(dtype) == 0;
   return sv::launch_chain(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+SV_EXPORT size_t sv_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
+                                                 sv_dtype dtype) {
+  if (!valid_dtype(dtype) || !chain_shape_ok(B, gamma, V)) return 0;
+  return sv::chain_layout(B, gamma, V).total;
+}
+
+SV_EXPORT sv_status sv_verify_chain(const void* target_logits, const void* draft_logits,
+                                    sv_dtype dtype, const int32_t* draft_tokens,
+                                    const float* uniforms, const float* temperature, int32_t B,
+                                    int32_t gamma, int64_t V, int32_t* out_tokens,
+                                    int32_t* out_num_accepted, float* out_p, float* out_q,
+                                    int32_t* out_status, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, temperature, B,
+                      gamma, V, out_tokens, out_num_accepted, out_p, out_q, out_status, nullptr,
+                      workspace, workspace_bytes, stream);
+}
+
+SV_EXPORT size_t sv_verify_chain_with_rates_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
+                                                            sv_dtype dtype) {
+  if (!valid_dtype(dtype) || !chain_shape_ok(B, gamma, V)) return 0;
+  return sv::chain_layout(B, gamma, V, true).total;
+}
+
+SV_EXPORT sv_status sv_verify_chain_with_rates(
+    const void* target_logits, const void* draft_logits, sv_dtype dtype,
+    const int32_t* draft_tokens, const float* uniforms, const float* temperature, int32_t B,
+    int32_t gamma, int64_t V, int32_t* out_tokens, int32_t* out_num_accepted, float* out_p,
+    float* out_q, int32_t* out_status, float* out_alpha, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  if (!out_alpha) return SV_ERR_NULL;
+  return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, temperature, B,
+                      gamma, V, out_tokens, out_num_accepted, out_p, out_q, out_status, out_alpha,
+                      workspace, workspace_bytes, stream);
 }
 
 SV_EXPORT size_t sv_verify_tree_workspace_bytes(int32_t n_trees, int32_t n_nodes, int64_t V,

@@ -703,9 +703,12 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
 // ------------------------------------------------------------------------------------ alpha
 
 // Acceptance rate alpha_i = sum_x min(p_i(x), q_i(x)) of position i of sequence b (the Step 3
-// accept probability averaged over x ~ q_i).  The sweep that produced the partials covered rows
-// [target 0..gamma-1, draft 0..gamma-1] of every sequence.  Three kernels follow it:
-//   merge    one wave per row merges its chunk partials into (M, S).
+// accept probability averaged over x ~ q_i).  They follow a sweep whose partials hold, per
+// sequence, tgt_rows target rows then gamma draft rows: target row i is partial row
+// b * (tgt_rows + gamma) + i and draft row i is that plus tgt_rows (tgt_rows = gamma for the
+// standalone acceptance rates, gamma + 1 when they follow chain verification, whose decide
+// kernel has already merged the rows).  Kernels:
+//   merge    one wave per row merges its chunk partials into (M, S) (standalone only).
 //   overlap  one wave per (b, i, chunk c) adds s * sum_x min(ra e_t(x), rb e_d(x)) over chunk c
 //            of target row i and draft row i, where e_t, e_d are the chunk-local softmax terms,
 //            A and B the chunk scales taking them to p and q, s = max(A, B) and
@@ -718,11 +721,15 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
 //   reduce   one wave per (b, i) adds the chunk sums in a fixed order (deterministic).
 constexpr int kAlphaBlock = 256;
 
+__device__ __forceinline__ int64_t alpha_target_row(const ChainParams& p, int64_t b, int i) {
+  return b * (p.tgt_rows + p.gamma) + i;
+}
+
 __global__ __launch_bounds__(kAlphaBlock) void k_chain_alpha_merge(ChainParams p, int64_t rows) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t r = int64_t(blockIdx.x) * (kAlphaBlock / kWave) + wave_id();
   if (r >= rows) return;  // wave-uniform
-  const int64_t b = r / (2 * p.gamma);
+  const int64_t b = r / (p.tgt_rows + p.gamma);
   const double Td = effective_temperature(uniform_load(p.temp, b));
   const RowStat st = merge_row(p.part + r * p.nchunk, p.nchunk, lane, Td);
   if (lane == 0) p.rowstat[r] = st;
@@ -740,7 +747,7 @@ __global__ __launch_bounds__(kStreamBlock<T>) void k_chain_alpha(ChainParams p, 
   const int64_t c = w - pair * nchunk;
   const int64_t b = pair / gamma;
   const int i = int(pair - b * gamma);
-  const int64_t jt = b * (2 * gamma) + i, jd = jt + gamma;  // rows of the partials
+  const int64_t jt = alpha_target_row(p, b, i), jd = jt + p.tgt_rows;  // rows of the partials
   const int nvalid = chunk_valid(V, c);
   RawChunk<T, VW> rt, rd;
   load_raw<T, VW>(static_cast<const T*>(p.tgt) + (b * (gamma + 1) + i) * V + c * kChunk, nvalid,
@@ -780,7 +787,7 @@ __global__ __launch_bounds__(kAlphaBlock) void k_chain_alpha_reduce(ChainParams 
   const int gamma = p.gamma;
   const int64_t nchunk = p.nchunk;
   const int64_t b = pair / gamma;
-  const int64_t jt = b * (2 * gamma) + (pair - b * gamma), jd = jt + gamma;
+  const int64_t jt = alpha_target_row(p, b, int(pair - b * gamma)), jd = jt + p.tgt_rows;
   const double* cs = chunk_sum + pair * nchunk;
   double acc = 0.0;
   for (int64_t c0 = 0; c0 < nchunk; c0 += int64_t(kWave) * kMergeBatch) {
@@ -806,6 +813,24 @@ __global__ __launch_bounds__(kAlphaBlock) void k_chain_alpha_reduce(ChainParams 
   }
 }
 
+// Overlap and reduce launches shared by the standalone acceptance rates and chain verification
+// with rates (partials and row statistics already in the workspace).
+template <typename T, int VW>
+hipError_t launch_alpha_tail(const ChainParams& p, int64_t B, double* chunk_sum,
+                             float* out_alpha, int32_t* out_status, hipStream_t s) {
+  const int64_t pairs = B * p.gamma;
+  const int64_t owaves = pairs * p.nchunk;
+  constexpr int wpb = kStreamBlock<T> / kWave;
+  hipError_t e = launch_kernel("alpha_overlap", k_chain_alpha<T, VW>,
+                               dim3(unsigned((owaves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
+                               p, chunk_sum, owaves);
+  if (e != hipSuccess) return e;
+  constexpr int awpb = kAlphaBlock / kWave;
+  return launch_kernel("alpha_reduce", k_chain_alpha_reduce,
+                       dim3(unsigned((pairs + awpb - 1) / awpb)), dim3(kAlphaBlock), s, p,
+                       chunk_sum, pairs, out_alpha, out_status);
+}
+
 template <typename T, int VW>
 hipError_t run_alpha(const AlphaArgs& a, hipStream_t s) {
   const AlphaLayout L = alpha_layout(a.B, a.gamma, a.V);
@@ -819,7 +844,6 @@ hipError_t run_alpha(const AlphaArgs& a, hipStream_t s) {
   p.nchunk = L.nchunk;
   p.part = reinterpret_cast<RowPart*>(a.ws + L.off_part);
   p.rowstat = reinterpret_cast<RowStat*>(a.ws + L.off_rowstat);
-  double* chunk_sum = reinterpret_cast<double*>(a.ws + L.off_chunk_sum);
   const int64_t rows = int64_t(a.B) * (2 * a.gamma);
   const int64_t total = rows * L.nchunk;
   const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
@@ -832,15 +856,8 @@ hipError_t run_alpha(const AlphaArgs& a, hipStream_t s) {
   e = launch_kernel("alpha_merge", k_chain_alpha_merge, dim3(unsigned((rows + awpb - 1) / awpb)),
                     dim3(kAlphaBlock), s, p, rows);
   if (e != hipSuccess) return e;
-  const int64_t pairs = int64_t(a.B) * a.gamma;
-  const int64_t owaves = pairs * L.nchunk;
-  e = launch_kernel("alpha_overlap", k_chain_alpha<T, VW>,
-                    dim3(unsigned((owaves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s, p,
-                    chunk_sum, owaves);
-  if (e != hipSuccess) return e;
-  return launch_kernel("alpha_reduce", k_chain_alpha_reduce,
-                       dim3(unsigned((pairs + awpb - 1) / awpb)), dim3(kAlphaBlock), s, p,
-                       chunk_sum, pairs, a.out_alpha, a.out_status);
+  return launch_alpha_tail<T, VW>(p, a.B, reinterpret_cast<double*>(a.ws + L.off_chunk_sum),
+                                  a.out_alpha, a.out_status, s);
 }
 
 // ------------------------------------------------------------------------------------ sampler
@@ -941,7 +958,8 @@ inline bool use_fused(const ChainArgs& a, int64_t nchunk, size_t elem_bytes) {
 
 template <typename T, int VW>
 hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
-  const ChainLayout L = chain_layout(a.B, a.gamma, a.V);
+  const bool with_rates = a.out_alpha != nullptr;
+  const ChainLayout L = chain_layout(a.B, a.gamma, a.V, with_rates);
   ChainParams p;
   p.tgt = a.target;
   p.drf = a.draft;
@@ -963,7 +981,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   p.out_status = a.out_status;
 
   if constexpr (VW > 1) {  // the one-element-load forms would spill; they take the split path
-    if (use_fused(a, L.nchunk, sizeof(T)))
+    if (!with_rates && use_fused(a, L.nchunk, sizeof(T)))  // the rates need the workspace partials
       return launch_kernel_shm("chain_fused", k_chain_fused<T, VW>, dim3(unsigned(a.B)),
                                dim3(kFusedBlock), fused_lds_bytes(a.gamma, L.nchunk), s, p);
   }
@@ -982,7 +1000,10 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   e = launch_kernel("chain_residual", k_chain_residual<T, VW>,
                     dim3(unsigned((rtotal + rw - 1) / rw)), dim3(kResidualBlock), s, p, rtotal);
   if (e != hipSuccess) return e;
-  return launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s, p);
+  e = launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s, p);
+  if (e != hipSuccess || !with_rates) return e;
+  return launch_alpha_tail<T, VW>(p, a.B, reinterpret_cast<double*>(a.ws + L.off_alpha_sum),
+                                  a.out_alpha, nullptr, s);
 }
 
 }  // namespace

@@ -67,12 +67,13 @@ inline int64_t groups_per_unit(int64_t rows_per_unit, int64_t V) {
 
 // Workspace: per (row, chunk) partials, per row statistics, per sequence decisions, per
 // (sequence, chunk) residual masses.  Every entry is written before it is read within a call.
+// with_rates: also the per (sequence, position, chunk) overlap sums of the acceptance rates.
 struct ChainLayout {
   int64_t nchunk;
-  size_t off_part, off_rowstat, off_seq, off_wres, total;
+  size_t off_part, off_rowstat, off_seq, off_wres, off_alpha_sum, total;
 };
 
-inline ChainLayout chain_layout(int64_t B, int64_t gamma, int64_t V) {
+inline ChainLayout chain_layout(int64_t B, int64_t gamma, int64_t V, bool with_rates = false) {
   ChainLayout L;
   L.nchunk = n_chunks(V);
   const int64_t rows = B * (2 * gamma + 1);
@@ -85,6 +86,8 @@ inline ChainLayout chain_layout(int64_t B, int64_t gamma, int64_t V) {
   off += align256(sizeof(SeqDecision) * size_t(B));
   L.off_wres = off;
   off += align256(sizeof(double) * size_t(B) * size_t(L.nchunk));
+  L.off_alpha_sum = off;
+  if (with_rates) off += align256(sizeof(double) * size_t(B) * size_t(gamma) * size_t(L.nchunk));
   L.total = off;
   return L;
 }
@@ -209,6 +212,7 @@ struct ChainArgs {
   float* out_p;
   float* out_q;
   int32_t* out_status;
+  float* out_alpha;  // [B, gamma] acceptance rates, or NULL (plain verification)
   char* ws;
   bool vec;  // 16-byte vector-load path is legal
 };

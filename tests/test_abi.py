@@ -58,6 +58,10 @@ def test_workspace_sizes():
     h = lib.sv_verify_chain_greedy_workspace_bytes
     assert h(256, 7, 152064, BD.SV_F32) >= 256 * 8 * 75 * 16
     assert h(1, 65, 1000, BD.SV_F32) == 0 and h(0, 4, 1000, BD.SV_BF16) == 0
+    r = lib.sv_verify_chain_with_rates_workspace_bytes
+    # the chain workspace plus one fp64 overlap sum per (sequence, position, chunk)
+    assert r(256, 7, 152064, BD.SV_F32) >= f(256, 7, 152064, BD.SV_F32) + 256 * 7 * 75 * 8
+    assert r(1, 65, 1000, BD.SV_F32) == 0 and r(1, 4, 1000, 7) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
@@ -95,6 +99,36 @@ def test_chain_null_pointers(field):
 ])
 def test_chain_validation(kw, status):
     assert chain_call(**kw) == status
+
+
+def rates_call(**kw):
+    a = dict(target=FAKE, draft=FAKE, dtype=BD.SV_F32, toks=FAKE, uni=FAKE, temp=FAKE, B=1,
+             gamma=4, V=1000, out_tokens=FAKE, out_nacc=FAKE, out_p=None, out_q=None,
+             out_status=None, out_alpha=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return BD.load().sv_verify_chain_with_rates(*a.values())
+
+
+@pytest.mark.parametrize("field", ["target", "draft", "toks", "uni", "temp", "out_tokens",
+                                   "out_nacc", "out_alpha"])
+def test_chain_with_rates_null_pointers(field):
+    assert rates_call(**{field: None}) == BD.SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), BD.SV_ERR_DTYPE), (dict(gamma=65), BD.SV_ERR_SHAPE),
+    (dict(V=0), BD.SV_ERR_SHAPE), (dict(ws=None), BD.SV_ERR_WORKSPACE),
+    (dict(ws_bytes=16), BD.SV_ERR_WORKSPACE),
+])
+def test_chain_with_rates_validation(kw, status):
+    assert rates_call(**kw) == status
+
+
+def test_chain_with_rates_needs_its_own_workspace_size():
+    lib = BD.load()
+    plain = lib.sv_verify_chain_workspace_bytes(4, 5, 9000, BD.SV_BF16)
+    assert lib.sv_verify_chain_with_rates_workspace_bytes(4, 5, 9000, BD.SV_BF16) > plain
+    assert rates_call(B=4, gamma=5, V=9000, dtype=BD.SV_BF16, ws_bytes=plain) == BD.SV_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("field", ["logits", "parents", "tokens", "out_path", "out_tokens",

@@ -84,3 +84,61 @@ def test_gamma_64_and_deterministic():
     check_acceptance_rates(b, first)
     again = run_alpha(b)
     assert np.array_equal(first["alpha"], again["alpha"], equal_nan=True)
+
+
+def run_with_rates(batch, offset=0):
+    d = BD.chain_to_device(batch)
+    t, dr = d["target"], d["draft"]
+    if offset:
+        def shifted(x):
+            flat = torch.empty(x.numel() + offset, dtype=x.dtype, device=x.device)
+            v = flat[offset:].view(x.shape)
+            v.copy_(x)
+            return v
+        t, dr = shifted(t), shifted(dr)
+    both = BD.sv_verify_chain(t, dr, d["draft_tokens"], d["uniforms"], d["temperature"],
+                              want_rates=True)
+    plain = BD.sv_verify_chain(t, dr, d["draft_tokens"], d["uniforms"], d["temperature"])
+    alone = BD.sv_chain_acceptance_rates(t, dr, d["temperature"])
+    torch.cuda.synchronize()
+    host = lambda o: {k: v.cpu().numpy() for k, v in o.items()}
+    return host(both), host(plain), host(alone)
+
+
+def _same(a, b, keys):
+    for k in keys:
+        assert np.array_equal(a[k], b[k], equal_nan=a[k].dtype.kind == "f"), k
+
+
+@pytest.mark.parametrize("dtype,B,gamma,V,offset", [
+    ("bf16", 5, 4, 5003 - 3, 0), ("f32", 4, 7, 4100, 0), ("bf16", 3, 5, 9001, 3),
+    ("f32", 2, 64, 300, 0)])
+def test_verify_with_rates_matches_both_calls(dtype, B, gamma, V, offset):
+    """sv_verify_chain_with_rates gives sv_verify_chain's outputs and sv_chain_acceptance_rates'
+    alpha bit for bit, and the alpha agrees with the oracle."""
+    b = I.chain_gaussian(50 + gamma, B, gamma, V, dtype, 2.0, 1.0, 0.9)
+    both, plain, alone = run_with_rates(b, offset)
+    _same(both, plain, ("tokens", "num_accepted", "p", "q", "status"))
+    _same(both, alone, ("alpha",))
+    check_acceptance_rates(b, {"alpha": both["alpha"]})
+
+
+def test_verify_with_rates_special_rows():
+    b = I.chain_gaussian(61, 6, 4, 3000, "f32", 2.0, 1.0, 1.0)
+    b.target[1, 2, 17] = np.nan          # target row 2 of sequence 1: alpha_2 NaN, fallback
+    b.draft[2, 0, :] = -np.inf           # a draft row without softmax
+    b.temperature[3] = 0.0               # bad temperature: fallback, rates still computed at T = 1
+    b.target[4, :, 100:] = -np.inf       # masked logits
+    both, plain, alone = run_with_rates(b)
+    _same(both, plain, ("tokens", "num_accepted", "p", "q", "status"))
+    _same(both, alone, ("alpha",))
+    assert np.isnan(both["alpha"][1, 2]) and np.isnan(both["alpha"][2, 0])
+    check_acceptance_rates(b, {"alpha": both["alpha"]})
+
+
+def test_verify_with_rates_full_size():
+    """The fp32 B=256 gamma=7 V=152064 workload: the combined call against the two separate ones."""
+    b = I.chain_b256_v152064()
+    both, plain, alone = run_with_rates(b)
+    _same(both, plain, ("tokens", "num_accepted", "p", "q", "status"))
+    _same(both, alone, ("alpha",))
