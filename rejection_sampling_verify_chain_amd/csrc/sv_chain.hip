@@ -353,6 +353,57 @@ struct Located {
   double total;
 };
 
+// One batch of the search: lane l holds the masses v of chunks base + l * kLocateBatch + i.
+// Given the running sum `carry` of the earlier batches, finds the first chunk whose running sum
+// exceeds tau (hit), and otherwise updates the last chunk with positive mass; returns the
+// batch's total mass.
+struct LocateState {
+  int64_t last_c = -1;
+  double last_before = 0.0;
+  bool hit = false;
+  Located at{0, 0.0, 0.0};
+};
+
+__device__ __forceinline__ double locate_batch(const double (&v)[kLocateBatch], int64_t base,
+                                               int lane, double carry, double tau, double total,
+                                               LocateState& ls_state) {
+  constexpr int NB = kLocateBatch;
+  double ls = 0.0;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) ls += v[i];
+  const double incl = wave_inclusive_scan(ls, lane);
+  double run = carry + (incl - ls);
+  int64_t cand = -1, lp = -1;
+  double cand_before = 0.0, lp_before = 0.0;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int64_t c = base + int64_t(lane) * NB + i;
+    const double prev = run;
+    run += v[i];
+    if (v[i] > 0.0) {
+      lp = c;
+      lp_before = prev;
+      if (cand < 0 && run > tau) {
+        cand = c;
+        cand_before = prev;
+      }
+    }
+  }
+  const uint64_t hit = __ballot(cand >= 0);
+  if (hit) {
+    const int L = __builtin_ctzll(hit);
+    ls_state.hit = true;
+    ls_state.at = Located{__shfl(cand, L, kWave), wave_broadcast(cand_before, L), total};
+  }
+  const uint64_t pos = __ballot(lp >= 0);
+  if (pos) {
+    const int L = 63 - __builtin_clzll(pos);
+    ls_state.last_c = __shfl(lp, L, kWave);
+    ls_state.last_before = wave_broadcast(lp_before, L);
+  }
+  return wave_broadcast(incl, kWave - 1);
+}
+
 template <typename MassFn>
 __device__ Located locate_chunk(int64_t nchunk, int lane, double u, MassFn mass) {
   constexpr int NB = kLocateBatch;
@@ -373,48 +424,32 @@ __device__ Located locate_chunk(int64_t nchunk, int lane, double u, MassFn mass)
   const double total = carry;
   const double tau = u * total;
   carry = 0.0;
-  int64_t last_c = -1;
-  double last_before = 0.0;
+  LocateState st;
   for (int64_t base = 0; base < nchunk; base += per) {
-    double ls = 0.0;
+    if (!single) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int64_t c = base + int64_t(lane) * NB + i;
-      if (!single) v[i] = c < nchunk ? mass(c) : 0.0;
-      ls += v[i];
-    }
-    const double incl = wave_inclusive_scan(ls, lane);
-    double run = carry + (incl - ls);
-    int64_t cand = -1, lp = -1;
-    double cand_before = 0.0, lp_before = 0.0;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int64_t c = base + int64_t(lane) * NB + i;
-      const double prev = run;
-      run += v[i];
-      if (v[i] > 0.0) {
-        lp = c;
-        lp_before = prev;
-        if (cand < 0 && run > tau) {
-          cand = c;
-          cand_before = prev;
-        }
+      for (int i = 0; i < NB; ++i) {
+        const int64_t c = base + int64_t(lane) * NB + i;
+        v[i] = c < nchunk ? mass(c) : 0.0;
       }
     }
-    const uint64_t hit = __ballot(cand >= 0);
-    if (hit) {
-      const int L = __builtin_ctzll(hit);
-      return Located{__shfl(cand, L, kWave), wave_broadcast(cand_before, L), total};
-    }
-    const uint64_t pos = __ballot(lp >= 0);
-    if (pos) {
-      const int L = 63 - __builtin_clzll(pos);
-      last_c = __shfl(lp, L, kWave);
-      last_before = wave_broadcast(lp_before, L);
-    }
-    carry += wave_broadcast(incl, kWave - 1);
+    carry += locate_batch(v, base, lane, carry, tau, total, st);
+    if (st.hit) return st.at;
   }
-  return Located{last_c < 0 ? 0 : last_c, last_before, total};
+  return Located{st.last_c < 0 ? 0 : st.last_c, st.last_before, total};
+}
+
+// The same search over a row of at most 64 * kLocateBatch chunks whose masses the lanes already
+// hold: v[i] = mass of chunk lane * kLocateBatch + i (0 past the row).
+__device__ Located locate_chunk_held(const double (&v)[kLocateBatch], int lane, double u) {
+  double ls = 0.0;
+#pragma unroll
+  for (int i = 0; i < kLocateBatch; ++i) ls += v[i];
+  const double total = wave_broadcast(wave_inclusive_scan(ls, lane), kWave - 1);
+  LocateState st;
+  locate_batch(v, 0, lane, 0.0, u * total, total, st);
+  if (st.hit) return st.at;
+  return Located{st.last_c < 0 ? 0 : st.last_c, st.last_before, total};
 }
 
 // Where the draw finds a sequence's row statistics, chunk partials and residual masses.
@@ -865,22 +900,52 @@ hipError_t run_alpha(const AlphaArgs& a, hipStream_t s) {
 // Draft-side sampler, one wave per logit row r: merges the row's chunk partials into (M, S),
 // locates the chunk holding u * W from the chunk masses and rescans it in token order (the
 // inverse CDF of the bonus draw), and evaluates p(y) in fp64.  Rows with a bad temperature,
-// a bad uniform or no softmax take token 0.
+// a bad uniform or no softmax take token 0.  For rows of up to 64 * kLocateBatch chunks the
+// partials are loaded once and both the merge and the chunk masses come from those registers,
+// and z(y) is taken from the rescanned chunk: two dependent memory round trips in all.
 template <typename T, int VW>
 __global__ __launch_bounds__(kWave) void k_sample_draw(ChainParams p, const float* uni,
                                                       int32_t* out_tokens, float* out_prob,
                                                       int32_t* out_status) {
+  constexpr int NB = kLocateBatch;
   const int64_t r = blockIdx.x;
   const int lane = threadIdx.x;
   const int64_t V = p.V, nchunk = p.nchunk;
   const T* row = static_cast<const T*>(p.tgt) + r * V;
-  const float tb = p.temp[r];
+  const float tb = uniform_load(p.temp, r);
   const float te = effective_temperature(tb);
   const double Td = te;
   const float kk = log2e_over_t(te);
+  const float uf = uniform_load(uni, r);
   const RowPart* pp = p.part + r * nchunk;
-  const RowStat st = merge_row(pp, nchunk, lane, Td);
-  const float uf = uni[r];
+  const bool held = nchunk <= int64_t(kWave) * NB;  // uniform
+
+  RowStat st;
+  double w[NB];  // held rows: mass of chunk lane * NB + i
+  if (held) {
+    RowPart q[NB];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t c = int64_t(lane) * NB + i;
+      q[i] = c < nchunk ? pp[c] : RowPart{-INFINITY, 0, 0.0};
+      mloc = fmaxf(mloc, q[i].m);
+    }
+    const float m = wave_max(mloc);
+    const bool finite_max = (m > -INFINITY) && (m < INFINITY);
+    double f[NB], s = 0.0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      f[i] = q[i].m == -INFINITY ? 0.0 : exp((double(q[i].m) - double(m)) / Td);
+      s += q[i].s * f[i];  // a NaN partial survives the zero factor
+    }
+    s = finite_max ? wave_sum(s) : 0.0;
+    st = RowStat{m, finite_max && (s > 0.0) && (s < INFINITY), s};
+#pragma unroll
+    for (int i = 0; i < NB; ++i) w[i] = q[i].s * (f[i] / s);  // q.s * chunk_scale
+  } else {
+    st = merge_row(pp, nchunk, lane, Td);
+  }
   int status = 0;
   if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
   if (!(uf >= 0.0f && uf < 1.0f)) status |= SV_ROW_BAD_UNIFORM;
@@ -889,18 +954,29 @@ __global__ __launch_bounds__(kWave) void k_sample_draw(ChainParams p, const floa
   double prob = NAN;
   if (status == 0) {
     const double u = uf;
-    const Located at = locate_chunk(nchunk, lane, u, [&](int64_t c) {
-      const RowPart q = pp[c];
-      return q.s * chunk_scale(q.m, st, Td);
-    });
-    const RowPart pc = pp[at.chunk];
+    const Located at = held ? locate_chunk_held(w, lane, u)
+                            : locate_chunk(nchunk, lane, u, [&](int64_t c) {
+                                const RowPart q = pp[c];
+                                return q.s * chunk_scale(q.m, st, Td);
+                              });
+    const int nvalid = chunk_valid(V, at.chunk);
+    RawChunk<T, VW> raw;
+    load_raw<T, VW>(row + at.chunk * kChunk, nvalid, lane, raw);
+    const RowPart pc = uniform_load(pp, at.chunk);
     const double scale = chunk_scale(pc.m, st, Td);
     float z[kElemsPerLane];
-    load_chunk<T, VW>(row, V, at.chunk, lane, z);
+    unpack_chunk<T, VW>(raw, nvalid, lane, z);
     const double tau_loc = scale > 0.0 ? (u * at.total - at.before) / scale : 0.0;
     y = chunk_scan<VW>(at.chunk, V, lane, tau_loc,
                        [&](int i) { return double(softmax_term(z[i], pc.m, kk)); });
-    prob = exp((double(widen(row[y])) - double(st.m)) / Td) / st.s;
+    // z(y) from the lane that holds it: chunk offset o = (j * 64 + l) * VW + t.
+    const int o = int(y - at.chunk * kChunk);
+    const int slot = (o / (VW * kWave)) * VW + o % VW;
+    float zy = z[0];
+#pragma unroll
+    for (int i = 1; i < kElemsPerLane; ++i) zy = i == slot ? z[i] : zy;
+    zy = __shfl(zy, (o / VW) % kWave, kWave);
+    prob = exp((double(zy) - double(st.m)) / Td) / st.s;
   }
   if (lane == 0) {
     out_tokens[r] = int32_t(y);

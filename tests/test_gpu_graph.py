@@ -54,8 +54,10 @@ def _same(a, b):
         assert np.array_equal(a[k], b[k], equal_nan=np.issubdtype(a[k].dtype, np.floating)), k
 
 
-@pytest.mark.parametrize("dtype,B,gamma,V", [("bf16", 4, 4, 5000), ("f32", 3, 6, 4100)])
-def test_graph_chain(dtype, B, gamma, V):
+@pytest.mark.parametrize("dtype,B,gamma,V,rates", [("bf16", 4, 4, 5000, False),
+                                                   ("f32", 3, 6, 4100, False),
+                                                   ("bf16", 3, 5, 6000, True)])
+def test_graph_chain(dtype, B, gamma, V, rates):
     dev = torch.device("cuda:0")
     gen = lambda seed: I.chain_gaussian(seed, B, gamma, V, dtype, 2.0, 1.0, 0.8)
     d = BD.chain_to_device(gen(100), dev)
@@ -64,13 +66,18 @@ def test_graph_chain(dtype, B, gamma, V):
             "p": torch.empty((B, gamma), dtype=torch.float32, device=dev),
             "q": torch.empty((B, gamma), dtype=torch.float32, device=dev),
             "status": torch.empty((B,), dtype=torch.int32, device=dev)}
-    ws = BD.workspace(BD.chain_workspace_bytes(B, gamma, V, d["dtype"]), dev)
+    if rates:
+        outs["alpha"] = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        ws = BD.workspace(BD.chain_with_rates_workspace_bytes(B, gamma, V, d["dtype"]), dev)
+    else:
+        ws = BD.workspace(BD.chain_workspace_bytes(B, gamma, V, d["dtype"]), dev)
 
     def call():
         BD.sv_verify_chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"],
                            d["temperature"], out_tokens=outs["tokens"],
                            out_num_accepted=outs["num_accepted"], out_p=outs["p"],
-                           out_q=outs["q"], out_status=outs["status"], workspace_buf=ws)
+                           out_q=outs["q"], out_status=outs["status"],
+                           out_alpha=outs.get("alpha"), workspace_buf=ws)
 
     g = _capture(call)
     for seed in REPLAY_SEEDS:
@@ -80,10 +87,12 @@ def test_graph_chain(dtype, B, gamma, V):
         torch.cuda.synchronize()
         got = _host(outs)
         eager = _host(BD.sv_verify_chain(d["target"], d["draft"], d["draft_tokens"],
-                                         d["uniforms"], d["temperature"]))
+                                         d["uniforms"], d["temperature"], want_rates=rates))
         torch.cuda.synchronize()
         _same(got, eager)
         check_chain(batch, got)
+        if rates:
+            check_acceptance_rates(batch, {"alpha": got["alpha"]})
 
 
 def test_graph_tree():
