@@ -22,7 +22,6 @@ __device__ __forceinline__ bool arg_better(float v, int32_t i, float bv, int32_t
 // One wave merges the chunk partials of one logit row: the row's argmax (lowest index among
 // equal maxima) and whether the row holds a NaN.  Lanes take chunks, all loads of a batch in
 // flight together, then a butterfly reduction with the argmax order.
-constexpr int kMergeBatch = 4;
 
 __device__ __forceinline__ void merge_row_argmax(const ArgPart* pp, int64_t nchunk, int lane,
                                                  int32_t* g, int* nan) {

@@ -184,7 +184,6 @@ __device__ int64_t chunk_scan(int64_t c, int64_t V, int lane, double tau_loc, Te
 // One wave merges the chunk partials of one row into (M, S, valid): M = max_c m_c and
 // S = sum_c S_c exp((m_c - M)/T) in fp64.  Partials are fetched kMergeBatch per lane at a
 // time, all loads in flight together; rows of up to 64 * kMergeBatch chunks are read once.
-constexpr int kMergeBatch = 4;
 
 __device__ RowStat merge_row(const RowPart* pp, int64_t nchunk, int lane, double Td) {
   const bool single = nchunk <= int64_t(kWave) * kMergeBatch;

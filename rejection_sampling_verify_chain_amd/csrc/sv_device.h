@@ -141,16 +141,6 @@ __device__ __forceinline__ void unpack_chunk(const RawChunk<T, VW>& r, int nvali
   }
 }
 
-// The lane's share of chunk c of a row of V elements, widened.
-template <typename T, int VW>
-__device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t V, int64_t c, int lane,
-                                           float (&z)[kElemsPerLane]) {
-  RawChunk<T, VW> r;
-  const int nvalid = chunk_valid(V, c);
-  load_raw<T, VW>(row + c * kChunk, nvalid, lane, r);
-  unpack_chunk<T, VW>(r, nvalid, lane, z);
-}
-
 // ---------------------------------------------------------------------------- streaming waves
 //
 // The streaming kernels (softmax partials, argmax partials) give each wave 8 KiB of logits to
@@ -227,6 +217,10 @@ __device__ __forceinline__ void stream_wave(int64_t gw, int64_t total, int64_t n
   }
   proc(k0, r0);
 }
+
+// Per-lane batch of the partial merges: a lane takes kMergeBatch partials of a row at a time
+// with all their loads in flight, so rows of up to 64 * kMergeBatch chunks are read at once.
+constexpr int kMergeBatch = 4;
 
 // ---------------------------------------------------------------------------- wave collectives
 // All-lane reductions over a full wave (all 64 lanes active).  Inside each row of 16 lanes four

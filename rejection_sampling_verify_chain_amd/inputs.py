@@ -509,12 +509,22 @@ def kv_chain_b256_g7():
 
 # ----------------------------------------------------------------------------- token trees
 
-def random_tree(gen, n_nodes, vocab, max_branch=4, max_depth=8):
+def random_tree(gen, n_nodes, vocab, max_branch=4, max_depth=8, max_draws=10000):
     """Breadth-first token tree: each expanded node gets a uniform number of children in
     [1, max_branch] (nodes at max_depth are not expanded), truncated at n_nodes nodes.
     Child tokens are uniform on [0, vocab) and distinct among siblings.  A draw that runs
-    out of nodes to expand before n_nodes is discarded and drawn again."""
-    while True:
+    out of nodes to expand before n_nodes is discarded and drawn again, at most max_draws
+    times; a shape that no tree of that branching and depth can reach raises ValueError."""
+    b = min(max_branch, vocab)
+    capacity, level = 1, 1
+    for _ in range(max_depth):
+        if capacity >= n_nodes:
+            break
+        level *= b
+        capacity += level
+    if capacity < n_nodes:
+        raise ValueError(f"no tree of {n_nodes} nodes has branching <= {b} and depth <= {max_depth}")
+    for _ in range(max_draws):
         parents = [-1]
         depth = [0]
         tokens = [int(gen.integers(0, vocab))]
@@ -535,6 +545,8 @@ def random_tree(gen, n_nodes, vocab, max_branch=4, max_depth=8):
                 tokens.append(int(t))
         if len(parents) == n_nodes:
             return np.array(parents, dtype=np.int32), np.array(tokens, dtype=np.int32)
+    raise ValueError(f"no {n_nodes}-node tree drawn in {max_draws} draws (branching <= "
+                     f"{max_branch}, depth <= {max_depth})")
 
 
 def tree_random(seed, n_trees, n_nodes, V, dtype, sigma=2.0, boost=4.0, boost_prob=0.6,

@@ -94,3 +94,13 @@ def test_zipf_alpha_near_target():
             q = softmax_fp64(widen(b.draft[s, i], "bf16"), 1.0)
             vals.append(np.minimum(p, q).sum())
     assert abs(np.mean(vals) - 0.7) < 0.03
+
+
+def test_random_tree_rejects_unreachable_shapes():
+    g = np.random.default_rng(0)
+    with pytest.raises(ValueError):
+        I.random_tree(g, 74, 4096, max_branch=4, max_depth=2)   # at most 1 + 4 + 16 nodes
+    with pytest.raises(ValueError):
+        I.random_tree(g, 5, 1, max_branch=4, max_depth=3)      # one token: a chain of 4 at most
+    parents, tokens = I.random_tree(g, 21, 4096, max_branch=4, max_depth=8)
+    assert len(parents) == 21 and parents[0] == -1
