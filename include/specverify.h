@@ -104,10 +104,14 @@ const char* sv_status_string(sv_status status);
  * out_q are unspecified.
  * Any base pointer alignment is accepted; 16-byte-aligned logits with V a multiple of 4 (fp32)
  * or 8 (bf16) take the vector-load path.
- * Execution: up to 256 sequences of at most 256 KiB of logits each (vector-load path) run in a
- * single launch, one workgroup per sequence; larger problems take four launches.  Both give
- * bit-identical results.  The environment variable SPECVERIFY_CHAIN_PATH=fused or =split, read
- * on every call, forces one of them (testing and measurement).
+ * Execution (vector-load path; all give bit-identical results): one launch with one workgroup
+ * per sequence when a sequence has at most 256 KiB of logits and B <= 256, or when 192 <= B <=
+ * 256; else a sweep across the chip followed by one workgroup per sequence when B <= 512 and a
+ * sequence's residual re-read (2 * V elements) is at most 256 KiB; else four launches.  Rows
+ * that are not 16-byte aligned always take four launches.  The environment variable
+ * SPECVERIFY_CHAIN_PATH=fused, =finish or =split, read on every call, forces one of them where
+ * the sequence's partials fit the one-workgroup form's 32 KiB LDS budget (testing and
+ * measurement).
  * ---------------------------------------------------------------------------------------- */
 size_t sv_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int64_t V, sv_dtype dtype);
 

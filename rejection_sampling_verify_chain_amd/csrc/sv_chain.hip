@@ -643,6 +643,9 @@ __global__ __launch_bounds__(kWave) void k_chain_draw(ChainParams p) {
 // its 2*gamma+1 rows (a chunk per wave at a time), keeps the chunk partials, row statistics,
 // decision and residual masses in LDS, and separates the steps with workgroup barriers.  Each
 // step calls the same device functions as the multi-kernel path, so both give the same bits.
+// With SWEPT the rows were swept by chain_sweep across the whole chip, and the workgroup copies
+// the sequence's chunk partials into LDS instead (chain_finish: the sweep plus one launch for
+// the decide, residual and draw steps); it also stores the row statistics in the workspace.
 constexpr int kFusedBlock = 1024;
 constexpr int kFusedWaves = kFusedBlock / kWave;
 template <typename T>
@@ -653,7 +656,7 @@ struct FusedShared {
   SeqDecision d;
 };
 
-template <typename T, int VW>
+template <typename T, int VW, bool SWEPT>
 __global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
   extern __shared__ __align__(16) unsigned char fused_lds[];  // partials [R][nchunk], masses [nchunk]
   __shared__ FusedShared sh;
@@ -675,12 +678,16 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
   Drafted g{0, false, 0.0f, 0.0f};
   if (wave == 0) g = gather_drafted<T>(p, b, lane);
 
+  const int units = R * int(nchunk);  // fits in int: the LDS budget bounds it
+  if constexpr (SWEPT) {
+    const RowPart* part = p.part + b * int64_t(units);
+    for (int w = int(threadIdx.x); w < units; w += kFusedBlock) prt[w] = part[w];
+  } else {
   // Sweep: the chunk partials of every row (virtual row j as in chain_row), kFusedUnits
   // consecutive units per wave with all their loads in flight (8 KiB of logits; more spills at
   // the 128 registers a 1024-thread workgroup allows); a unit past the end reloads the last one
-  // and is not reduced.  Units fit in int: the LDS budget bounds them.
+  // and is not reduced.
   constexpr int U = kFusedUnits<T>;
-  const int units = R * int(nchunk);
   for (int w0 = wave * U; w0 < units; w0 += kFusedWaves * U) {
     RawChunk<T, VW> r[U];
 #pragma unroll
@@ -703,10 +710,14 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
       }
     }
   }
+  }
   __syncthreads();
   for (int j = wave; j < R; j += kFusedWaves) {
     const RowStat st = merge_row(prt + int64_t(j) * nchunk, nchunk, lane, Td);
-    if (lane == 0) sh.st[j] = st;
+    if (lane == 0) {
+      sh.st[j] = st;
+      if (SWEPT) p.rowstat[b * R + j] = st;
+    }
   }
   __syncthreads();
   if (wave == 0) {
@@ -1007,28 +1018,49 @@ hipError_t run_sample(const SampleArgs& a, hipStream_t s) {
                        s, p, a.uniforms, a.out_tokens, a.out_prob, a.out_status);
 }
 
-// Path choice for chain verification.  The one-workgroup path replaces four launches with one;
-// a workgroup streams about 128 KiB per memory round trip, so it wins while a sequence's rows
-// take at most two such rounds and the grid fits the chip in one wave of workgroups (measured:
-// B = 1, V = 8000 bf16, gamma = 4: 13.8 vs 20.5 us per call; V = 32000: 26.0 vs 20.7 us;
-// B = 256, V = 8000: 18.4 vs 27.2 us; B = 1024: 64 vs 56 us).  It needs the sequence's partials
-// and residual masses to fit its LDS budget.  SPECVERIFY_CHAIN_PATH=fused or =split forces a
-// path (for tests and measurement; "fused" still requires the LDS fit).
+// Path choice for chain verification (all three give the same bits):
+//   fused   one launch, one workgroup per sequence for every step;
+//   finish  the sweep across the chip, then one workgroup per sequence for decide, residual and
+//           draw (chain_finish);
+//   split   the sweep, then decide, residual and draw as three launches.
+// A 1024-thread workgroup (one per CU at its register count) streams about 128 KiB per memory
+// round trip.  So the fused path wins when a sequence's rows take at most two such rounds, or
+// when 192..256 sequences give every CU a workgroup and together they saturate HBM (the tails of
+// some sequences then overlap the sweeps of others).  The finish path wins while a sequence's
+// residual re-read (2 * V elements) stays small.  Measured per call, split / finish / fused:
+// B = 1, V = 1000 fp32: 20.2 / 15.6 / 13.4 us; B = 64, V = 32000 bf16: 27.2 / 24.7 / 33.8 us;
+// B = 256, V = 32000 bf16: 49.5 / 42.1 / 38.9 us; B = 256, gamma = 7, V = 152064 fp32:
+// 406.8 / 400.8 / 390.4 us; B = 64, V = 128256 bf16: 48.1 / 54.4 / 103.1 us; B = 1, V = 152064
+// fp32: 19.7 / 36.6 / 195.8 us; B = 1024, V = 32000 bf16: 141.4 / 144.0 / 145.0 us.
+// Both one-workgroup forms need the sequence's partials and residual masses to fit their LDS
+// budget; the rates need the sweep's partials in the workspace, so they take finish where fused
+// would be chosen.  SPECVERIFY_CHAIN_PATH=fused, =finish or =split forces a path (for tests and
+// measurement; subject to the LDS fit, and fused becomes finish with the rates).
+enum class ChainPath { kSplit, kFused, kFinish };
+
 constexpr size_t kFusedMaxLds = 32 * 1024;
-constexpr int64_t kFusedMaxSeqBytes = 256 * 1024;
-constexpr int kFusedMaxBatch = 256;
+constexpr int64_t kFusedMaxSeqBytes = 256 * 1024;    // small rows: fused for B <= 256
+constexpr int kChipFillMin = 192, kChipFillMax = 256;  // fused whatever the row size
+constexpr int64_t kFinishMaxResidualBytes = 256 * 1024;
+constexpr int kFinishMaxBatch = 512;
 
 inline size_t fused_lds_bytes(int gamma, int64_t nchunk) {
   return sizeof(RowPart) * size_t(2 * gamma + 1) * size_t(nchunk) + sizeof(double) * size_t(nchunk);
 }
 
-inline bool use_fused(const ChainArgs& a, int64_t nchunk, size_t elem_bytes) {
-  if (fused_lds_bytes(a.gamma, nchunk) > kFusedMaxLds) return false;
+inline ChainPath choose_path(const ChainArgs& a, int64_t nchunk, size_t elem_bytes,
+                             bool with_rates) {
+  if (fused_lds_bytes(a.gamma, nchunk) > kFusedMaxLds) return ChainPath::kSplit;
+  const ChainPath fused = with_rates ? ChainPath::kFinish : ChainPath::kFused;
   const char* e = getenv("SPECVERIFY_CHAIN_PATH");
-  if (e && strcmp(e, "fused") == 0) return true;
-  if (e && strcmp(e, "split") == 0) return false;
-  return a.B <= kFusedMaxBatch &&
-         int64_t(2 * a.gamma + 1) * a.V * int64_t(elem_bytes) <= kFusedMaxSeqBytes;
+  if (e && strcmp(e, "fused") == 0) return fused;
+  if (e && strcmp(e, "finish") == 0) return ChainPath::kFinish;
+  if (e && strcmp(e, "split") == 0) return ChainPath::kSplit;
+  const int64_t s = int64_t(elem_bytes);
+  if (a.B <= kChipFillMax && int64_t(2 * a.gamma + 1) * a.V * s <= kFusedMaxSeqBytes) return fused;
+  if (a.B >= kChipFillMin && a.B <= kChipFillMax) return fused;
+  if (a.B <= kFinishMaxBatch && 2 * a.V * s <= kFinishMaxResidualBytes) return ChainPath::kFinish;
+  return ChainPath::kSplit;
 }
 
 template <typename T, int VW>
@@ -1055,9 +1087,12 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   p.out_q = a.out_q;
   p.out_status = a.out_status;
 
-  if constexpr (VW > 1) {  // the one-element-load forms would spill; they take the split path
-    if (!with_rates && use_fused(a, L.nchunk, sizeof(T)))  // the rates need the workspace partials
-      return launch_kernel_shm("chain_fused", k_chain_fused<T, VW>, dim3(unsigned(a.B)),
+  // The one-element-load forms of the one-workgroup kernel would spill; they take the split path.
+  const ChainPath path =
+      VW > 1 ? choose_path(a, L.nchunk, sizeof(T), with_rates) : ChainPath::kSplit;
+  if constexpr (VW > 1) {
+    if (path == ChainPath::kFused)
+      return launch_kernel_shm("chain_fused", k_chain_fused<T, VW, false>, dim3(unsigned(a.B)),
                                dim3(kFusedBlock), fused_lds_bytes(a.gamma, L.nchunk), s, p);
   }
 
@@ -1068,6 +1103,15 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
                                dim3(unsigned((waves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
                                p, total);
   if (e != hipSuccess) return e;
+  if constexpr (VW > 1) {
+    if (path == ChainPath::kFinish) {
+      e = launch_kernel_shm("chain_finish", k_chain_fused<T, VW, true>, dim3(unsigned(a.B)),
+                            dim3(kFusedBlock), fused_lds_bytes(a.gamma, L.nchunk), s, p);
+      if (e != hipSuccess || !with_rates) return e;
+      return launch_alpha_tail<T, VW>(p, a.B, reinterpret_cast<double*>(a.ws + L.off_alpha_sum),
+                                      a.out_alpha, nullptr, s);
+    }
+  }
   e = launch_kernel("chain_decide", k_chain_decide<T, VW>, dim3(unsigned(a.B)), dim3(kBlock), s, p);
   if (e != hipSuccess) return e;
   const int64_t rtotal = int64_t(a.B) * L.nchunk;

@@ -86,7 +86,9 @@ def test_gamma_64_and_deterministic():
     assert np.array_equal(first["alpha"], again["alpha"], equal_nan=True)
 
 
-def run_with_rates(batch, offset=0):
+def run_with_rates(batch, offset=0, path=None, monkeypatch=None):
+    if path is not None:
+        monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", path)
     d = BD.chain_to_device(batch)
     t, dr = d["target"], d["draft"]
     if offset:
@@ -110,14 +112,15 @@ def _same(a, b, keys):
         assert np.array_equal(a[k], b[k], equal_nan=a[k].dtype.kind == "f"), k
 
 
+@pytest.mark.parametrize("path", ["finish", "split"])
 @pytest.mark.parametrize("dtype,B,gamma,V,offset", [
     ("bf16", 5, 4, 5003 - 3, 0), ("f32", 4, 7, 4100, 0), ("bf16", 3, 5, 9001, 3),
     ("f32", 2, 64, 300, 0)])
-def test_verify_with_rates_matches_both_calls(dtype, B, gamma, V, offset):
+def test_verify_with_rates_matches_both_calls(dtype, B, gamma, V, offset, path, monkeypatch):
     """sv_verify_chain_with_rates gives sv_verify_chain's outputs and sv_chain_acceptance_rates'
-    alpha bit for bit, and the alpha agrees with the oracle."""
+    alpha bit for bit, and the alpha agrees with the oracle (both chain paths it can take)."""
     b = I.chain_gaussian(50 + gamma, B, gamma, V, dtype, 2.0, 1.0, 0.9)
-    both, plain, alone = run_with_rates(b, offset)
+    both, plain, alone = run_with_rates(b, offset, path, monkeypatch)
     _same(both, plain, ("tokens", "num_accepted", "p", "q", "status"))
     _same(both, alone, ("alpha",))
     check_acceptance_rates(b, {"alpha": both["alpha"]})

@@ -17,11 +17,12 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-@pytest.fixture(autouse=True, params=["fused", "split"])
+@pytest.fixture(autouse=True, params=["fused", "finish", "split"])
 def chain_path(request, monkeypatch):
-    """Every test runs on both chain paths: the one-workgroup-per-sequence kernel (forced wherever
-    its LDS image fits; rows that are not 16-byte aligned always take the multi-kernel path) and
-    the multi-kernel path."""
+    """Every test runs on the three chain paths: one workgroup per sequence for every step, the
+    sweep followed by one workgroup per sequence for the rest (both forced wherever their LDS image
+    fits; rows that are not 16-byte aligned always take the multi-kernel path), and the
+    multi-kernel path."""
     monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", request.param)
     return request.param
 
@@ -203,13 +204,14 @@ def test_extreme_temperatures(T):
 @pytest.mark.parametrize("dtype,B,gamma,V,T", [("bf16", 3, 7, 32000, 0.8), ("f32", 5, 4, 5003, 1.0),
                                                 ("bf16", 2, 64, 300, 1.3)])
 def test_paths_bit_identical(dtype, B, gamma, V, T, monkeypatch):
-    """The two paths compute every step with the same device functions: all outputs agree bit for
-    bit (p and q included), on sequences that cut early, accept everything, and fall back."""
+    """The three paths compute every step with the same device functions: all outputs agree bit
+    for bit (p and q included), on sequences that cut early, accept everything, and fall back."""
     b = I.chain_gaussian(31, B, gamma, V, dtype, 2.0, 1.0, T)
     b.temperature[0] = -1.0  # a fallback sequence
     outs = {}
-    for path in ("fused", "split"):
+    for path in ("fused", "finish", "split"):
         monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", path)
         outs[path] = run_chain(b)
     for k in outs["split"]:
-        assert np.array_equal(outs["fused"][k], outs["split"][k], equal_nan=True), k
+        for path in ("fused", "finish"):
+            assert np.array_equal(outs[path][k], outs["split"][k], equal_nan=True), (path, k)

@@ -4,7 +4,7 @@ Each case draws its shape (batch, gamma, vocabulary, node count, row width), dty
 and logit scales from a fixed seed, builds the inputs with the seeded generators, and compares
 the library's outputs with the oracle by the same rules as the other parity tests.  The shapes
 cross the chunk (2048) and vector-width boundaries at random, including V = 1 and gamma = 1;
-chain cases run on both chain paths.
+chain cases run on all three chain paths.
 """
 
 import numpy as np
@@ -34,7 +34,7 @@ def _host(out):
     return {k: (None if v is None else v.cpu().numpy()) for k, v in out.items()}
 
 
-@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("path", ["fused", "finish", "split"])
 @pytest.mark.parametrize("case", CASES)
 def test_random_chain(case, path, monkeypatch):
     rng = _rng(1, case)
