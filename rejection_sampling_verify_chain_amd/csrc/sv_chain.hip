@@ -656,10 +656,11 @@ struct FusedShared {
   SeqDecision d;
 };
 
+// The body of chain_fused and chain_finish (all threads of the sequence's workgroup); fused_lds
+// is the launch's dynamic LDS: partials [R][nchunk], then residual masses [nchunk].
 template <typename T, int VW, bool SWEPT>
-__global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
-  extern __shared__ __align__(16) unsigned char fused_lds[];  // partials [R][nchunk], masses [nchunk]
-  __shared__ FusedShared sh;
+__device__ __forceinline__ void one_workgroup_chain(const ChainParams& p, unsigned char* fused_lds,
+                                                    FusedShared& sh) {
   const int64_t b = blockIdx.x;
   const int gamma = p.gamma;
   const int R = 2 * gamma + 1;
@@ -743,6 +744,20 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
   }
   if (wave != 0) return;
   draw_sequence<T, VW>(p, b, d, LdsSrc{sh.st, prt, wr, nchunk});
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
+  extern __shared__ __align__(16) unsigned char fused_lds[];
+  __shared__ FusedShared sh;
+  one_workgroup_chain<T, VW, false>(p, fused_lds, sh);
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kFusedBlock) void k_chain_finish(ChainParams p) {
+  extern __shared__ __align__(16) unsigned char fused_lds[];
+  __shared__ FusedShared sh;
+  one_workgroup_chain<T, VW, true>(p, fused_lds, sh);
 }
 
 // ------------------------------------------------------------------------------------ alpha
@@ -1092,7 +1107,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
       VW > 1 ? choose_path(a, L.nchunk, sizeof(T), with_rates) : ChainPath::kSplit;
   if constexpr (VW > 1) {
     if (path == ChainPath::kFused)
-      return launch_kernel_shm("chain_fused", k_chain_fused<T, VW, false>, dim3(unsigned(a.B)),
+      return launch_kernel_shm("chain_fused", k_chain_fused<T, VW>, dim3(unsigned(a.B)),
                                dim3(kFusedBlock), fused_lds_bytes(a.gamma, L.nchunk), s, p);
   }
 
@@ -1105,7 +1120,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   if constexpr (VW > 1) {
     if (path == ChainPath::kFinish) {
-      e = launch_kernel_shm("chain_finish", k_chain_fused<T, VW, true>, dim3(unsigned(a.B)),
+      e = launch_kernel_shm("chain_finish", k_chain_finish<T, VW>, dim3(unsigned(a.B)),
                             dim3(kFusedBlock), fused_lds_bytes(a.gamma, L.nchunk), s, p);
       if (e != hipSuccess || !with_rates) return e;
       return launch_alpha_tail<T, VW>(p, a.B, reinterpret_cast<double*>(a.ws + L.off_alpha_sum),
