@@ -123,6 +123,28 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
                           size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Chain verification with early exit ([SpS] Step 3: the tests run in order and stop at the first
+ * rejection, so the rows of later positions are never needed).
+ *
+ * Same arguments, workspace size (sv_verify_chain_workspace_bytes) and errors as
+ * sv_verify_chain.  For inputs whose logit rows are all finite (no NaN, no +inf, not all -inf)
+ * out_tokens, out_num_accepted and out_status equal sv_verify_chain's bit for bit, and so do
+ * out_p / out_q at positions i <= k; after the cut they are NaN where the row was not read and
+ * sv_verify_chain's values elsewhere.
+ * Rows after the cut may not be read: a non-finite value there may or may not set
+ * SV_ROW_NONFINITE and the fallback.  Batches of at least 128 sequences take positions in order
+ * in one launch, one workgroup per sequence, reading target and draft row i only while
+ * position i is reached (and target row gamma only if every draft is accepted); smaller batches
+ * run as sv_verify_chain.
+ * ---------------------------------------------------------------------------------------- */
+sv_status sv_verify_chain_lazy(const void* target_logits, const void* draft_logits,
+                               sv_dtype dtype, const int32_t* draft_tokens, const float* uniforms,
+                               const float* temperature, int32_t B, int32_t gamma, int64_t V,
+                               int32_t* out_tokens, int32_t* out_num_accepted, float* out_p,
+                               float* out_q, int32_t* out_status, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Chain verification with per-position acceptance rates ([SpS] Step 3 and expected speedup:
  * the accept probability alpha, watched in monitoring).
  *

@@ -29,6 +29,7 @@ EXPORTS = (
     "sv_version", "sv_status_string",
     "sv_verify_chain_workspace_bytes", "sv_verify_chain",
     "sv_verify_chain_with_rates_workspace_bytes", "sv_verify_chain_with_rates",
+    "sv_verify_chain_lazy",
     "sv_verify_tree_workspace_bytes", "sv_verify_tree",
     "sv_verify_chain_greedy_workspace_bytes", "sv_verify_chain_greedy",
     "sv_chain_acceptance_rates_workspace_bytes", "sv_chain_acceptance_rates",
@@ -66,6 +67,9 @@ def load():
     lib.sv_verify_chain.restype = ctypes.c_int
     lib.sv_verify_chain.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i64,
                                     vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sv_verify_chain_lazy.restype = ctypes.c_int
+    lib.sv_verify_chain_lazy.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i64,
+                                         vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sv_verify_chain_with_rates_workspace_bytes.restype = sz
     lib.sv_verify_chain_with_rates_workspace_bytes.argtypes = [i32, i32, i64, ctypes.c_int]
     lib.sv_verify_chain_with_rates.restype = ctypes.c_int
@@ -200,16 +204,19 @@ def workspace(nbytes, device):
 def sv_verify_chain(target, draft, draft_tokens, uniforms, temperature, *, out_tokens=None,
                     out_num_accepted=None, out_p=None, out_q=None, out_status=None,
                     workspace_buf=None, stream=None, want_pq=True, want_status=True,
-                    want_rates=False, out_alpha=None):
+                    want_rates=False, out_alpha=None, lazy=False):
     """Chain verification through the C ABI.
 
     target [B, gamma+1, V] and draft [B, gamma, V] (fp32 or bf16), draft_tokens int32
     [B, gamma], uniforms fp32 [B, gamma+1], temperature fp32 [B].  Returns a dict of the
     output tensors (tokens, num_accepted, p, q, status); the call is asynchronous.  With
     want_rates (or an out_alpha tensor) it calls sv_verify_chain_with_rates and the dict also
-    holds alpha fp32 [B, gamma].
+    holds alpha fp32 [B, gamma]; with lazy it calls sv_verify_chain_lazy (early exit).
     """
     lib = load()
+    rates = want_rates or out_alpha is not None
+    if rates and lazy:
+        raise ValueError("the early-exit entry point has no acceptance rates")
     if target.dtype not in _DTYPE:
         raise ValueError(f"logits must be float32 or bfloat16, got {target.dtype}")
     dev = target.device
@@ -228,7 +235,6 @@ def sv_verify_chain(target, draft, draft_tokens, uniforms, temperature, *, out_t
         out_q = _out(out_q, "out_q", torch.float32, (B, gamma), dev)
     if want_status or out_status is not None:
         out_status = _out(out_status, "out_status", torch.int32, (B,), dev)
-    rates = want_rates or out_alpha is not None
     if rates:
         out_alpha = _out(out_alpha, "out_alpha", torch.float32, (B, gamma), dev)
         need = chain_with_rates_workspace_bytes(B, gamma, V, target.dtype)
@@ -240,13 +246,15 @@ def sv_verify_chain(target, draft, draft_tokens, uniforms, temperature, *, out_t
             _ptr(temperature), B, gamma, V, _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_p),
             _ptr(out_q), _ptr(out_status)]
     if rates:
+        name = "sv_verify_chain_with_rates"
         st = lib.sv_verify_chain_with_rates(*args, _ptr(out_alpha), _ptr(workspace_buf),
                                             workspace_buf.numel(), _stream(stream))
     else:
-        st = lib.sv_verify_chain(*args, _ptr(workspace_buf), workspace_buf.numel(),
-                                 _stream(stream))
+        name = "sv_verify_chain_lazy" if lazy else "sv_verify_chain"
+        st = getattr(lib, name)(*args, _ptr(workspace_buf), workspace_buf.numel(),
+                                _stream(stream))
     if st != SV_OK:
-        raise SpecVerifyError(st, "sv_verify_chain_with_rates" if rates else "sv_verify_chain")
+        raise SpecVerifyError(st, name)
     out = {"tokens": out_tokens, "num_accepted": out_num_accepted, "p": out_p, "q": out_q,
            "status": out_status}
     if rates:

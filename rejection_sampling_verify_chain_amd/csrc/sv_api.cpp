@@ -76,7 +76,7 @@ sv_status verify_chain(const void* target_logits, const void* draft_logits, sv_d
                        const int32_t* draft_tokens, const float* uniforms,
                        const float* temperature, int32_t B, int32_t gamma, int64_t V,
                        int32_t* out_tokens, int32_t* out_num_accepted, float* out_p, float* out_q,
-                       int32_t* out_status, float* out_alpha, void* workspace,
+                       int32_t* out_status, float* out_alpha, bool lazy, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
   if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !temperature ||
       !out_tokens || !out_num_accepted)
@@ -103,6 +103,7 @@ sv_status verify_chain(const void* target_logits, const void* draft_logits, sv_d
   a.out_q = out_q;
   a.out_status = out_status;
   a.out_alpha = out_alpha;
+  a.lazy = lazy;
   a.ws = static_cast<char*>(workspace);
   a.vec = aligned16(target_logits) && aligned16(draft_logits) && V % vec_width(dtype) == 0;
   return sv::launch_chain(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
@@ -125,7 +126,19 @@ SV_EXPORT sv_status sv_verify_chain(const void* target_logits, const void* draft
                                     size_t workspace_bytes, hipStream_t stream) {
   return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, temperature, B,
                       gamma, V, out_tokens, out_num_accepted, out_p, out_q, out_status, nullptr,
-                      workspace, workspace_bytes, stream);
+                      false, workspace, workspace_bytes, stream);
+}
+
+SV_EXPORT sv_status sv_verify_chain_lazy(const void* target_logits, const void* draft_logits,
+                                         sv_dtype dtype, const int32_t* draft_tokens,
+                                         const float* uniforms, const float* temperature,
+                                         int32_t B, int32_t gamma, int64_t V, int32_t* out_tokens,
+                                         int32_t* out_num_accepted, float* out_p, float* out_q,
+                                         int32_t* out_status, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, temperature, B,
+                      gamma, V, out_tokens, out_num_accepted, out_p, out_q, out_status, nullptr,
+                      true, workspace, workspace_bytes, stream);
 }
 
 SV_EXPORT size_t sv_verify_chain_with_rates_workspace_bytes(int32_t B, int32_t gamma, int64_t V,
@@ -143,7 +156,7 @@ SV_EXPORT sv_status sv_verify_chain_with_rates(
   if (!out_alpha) return SV_ERR_NULL;
   return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, temperature, B,
                       gamma, V, out_tokens, out_num_accepted, out_p, out_q, out_status, out_alpha,
-                      workspace, workspace_bytes, stream);
+                      false, workspace, workspace_bytes, stream);
 }
 
 SV_EXPORT size_t sv_verify_tree_workspace_bytes(int32_t n_trees, int32_t n_nodes, int64_t V,

@@ -760,6 +760,201 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_finish(ChainParams p) {
   one_workgroup_chain<T, VW, true>(p, fused_lds, sh);
 }
 
+// ------------------------------------------------------------------------ early exit (positions in order)
+//
+// One workgroup per sequence takes the positions in order: it sweeps target row i and draft row
+// i into LDS, merges them, and tests position i; it stops at the first rejection (residual
+// masses over the same two rows, then the draw) or, after gamma accepts, sweeps target row gamma
+// for the bonus draw.  Rows after the cut are never read.  Each step calls the same device
+// functions as the other paths, so for inputs whose rows are all finite the outputs are theirs
+// bit for bit; only non-finite values in unread rows go unseen.
+
+// The draw's records for the row pair in LDS: slot 0 holds target row j <= gamma, slot 1 draft row
+// j > gamma.
+struct PairSrc {
+  const RowStat* st2;  // [2]
+  const RowPart* prt;  // [2][nchunk]
+  const double* wr;    // [nchunk]
+  int64_t nchunk;
+  int gamma;
+  __device__ int slot(int j) const { return j > gamma ? 1 : 0; }
+  __device__ RowStat stat(int j) const { return st2[slot(j)]; }
+  __device__ RowPart part(int j, int64_t c) const { return prt[slot(j) * nchunk + c]; }
+  __device__ RowPart part_lane(int j, int64_t c) const { return prt[slot(j) * nchunk + c]; }
+  __device__ double wres(int64_t c) const { return wr[c]; }
+};
+
+struct LazyShared {
+  RowStat st2[2];
+  int32_t state;  // after a position's test: 0 accepted, 1 rejected, 2 non-finite row
+  int32_t status;
+};
+
+// Chunk partials of rows j0 (slot 0) and, if nrows == 2, j1 (slot 1) into prt (all threads).
+template <typename T, int VW>
+__device__ __forceinline__ void sweep_pair(const ChainParams& p, int64_t b, int j0, int j1,
+                                           int nrows, RowPart* prt, float kk, int wave, int lane) {
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const int nchunk = int(p.nchunk);
+  constexpr int U = kFusedUnits<T>;
+  const int units = nrows * nchunk;
+  for (int w0 = wave * U; w0 < units; w0 += kFusedWaves * U) {
+    RawChunk<T, VW> r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = min(w0 + u, units - 1);
+      const int slot = w / nchunk;
+      const int c = w - slot * nchunk;
+      load_raw<T, VW>(chain_row(tgt, drf, b, p.gamma, slot ? j1 : j0, p.V) + int64_t(c) * kChunk,
+                      chunk_valid(p.V, c), lane, r[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = w0 + u;
+      if (w < units) {  // wave-uniform
+        const int c = w - (w / nchunk) * nchunk;
+        float z[kElemsPerLane];
+        unpack_chunk<T, VW>(r[u], chunk_valid(p.V, c), lane, z);
+        const RowPart rp = reduce_chunk(z, kk);
+        if (lane == 0) prt[w] = rp;
+      }
+    }
+  }
+}
+
+// The fallback result of sequence b (one wave): k = 0, tokens [0, -1, ...], p and q NaN.
+__device__ __forceinline__ void write_fallback(const ChainParams& p, int64_t b, int status,
+                                               int lane) {
+  for (int i = lane; i <= p.gamma; i += kWave) p.out_tokens[b * (p.gamma + 1) + i] = i == 0 ? 0 : -1;
+  for (int i = lane; i < p.gamma; i += kWave) {
+    if (p.out_p) p.out_p[b * p.gamma + i] = NAN;
+    if (p.out_q) p.out_q[b * p.gamma + i] = NAN;
+  }
+  if (lane == 0) {
+    p.out_nacc[b] = 0;
+    if (p.out_status) p.out_status[b] = status;
+  }
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kFusedBlock) void k_chain_lazy(ChainParams p) {
+  extern __shared__ __align__(16) unsigned char lazy_lds[];  // partials [2][nchunk], masses [nchunk]
+  __shared__ LazyShared sh;
+  const int64_t b = blockIdx.x;
+  const int gamma = p.gamma;
+  const int64_t V = p.V, nchunk = p.nchunk;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & (kWave - 1);
+  RowPart* prt = reinterpret_cast<RowPart*>(lazy_lds);
+  double* wr = reinterpret_cast<double*>(lazy_lds + sizeof(RowPart) * 2 * size_t(nchunk));
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const float tb = uniform_load(p.temp, b);
+  const float te = effective_temperature(tb);
+  const double Td = te;
+  const float kk = log2e_over_t(te);
+
+  // Checks that read no logit row: temperature, uniforms, draft tokens.
+  Drafted g{0, false, 0.0f, 0.0f};
+  if (wave == 0) {
+    g = gather_drafted<T>(p, b, lane);
+    int status = 0;
+    if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
+    bool bad = false;
+    for (int i = lane; i <= gamma; i += kWave) {
+      const float u = p.uni[b * (gamma + 1) + i];
+      bad |= !(u >= 0.0f && u < 1.0f);
+    }
+    if (__any(bad)) status |= SV_ROW_BAD_UNIFORM;
+    if (__any(g.bad)) status |= SV_ROW_TOKEN_RANGE;
+    if (lane == 0) sh.status = status;
+  }
+  __syncthreads();
+  if (sh.status != 0) {  // the whole workgroup
+    if (wave == 0) write_fallback(p, b, sh.status, lane);
+    return;
+  }
+
+  int k = gamma;
+  for (int i = 0; i < gamma; ++i) {
+    sweep_pair<T, VW>(p, b, i, gamma + 1 + i, 2, prt, kk, wave, lane);
+    __syncthreads();
+    if (wave < 2) {
+      const RowStat st = merge_row(prt + wave * nchunk, nchunk, lane, Td);
+      if (lane == 0) sh.st2[wave] = st;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const RowStat a = sh.st2[0], d = sh.st2[1];
+      int state = 2;
+      if (a.valid && d.valid) {
+        // Position i's test, on the logits lane i gathered (the eager path's arithmetic).
+        const double zt = __shfl(g.zt, i, kWave), zd = __shfl(g.zd, i, kWave);
+        const double pi = exp((zt - double(a.m)) / Td) / a.s;
+        const double qi = exp((zd - double(d.m)) / Td) / d.s;
+        const double u = p.uni[b * (gamma + 1) + i];
+        const bool accept = qi > 0.0 ? u < fmin(1.0, pi / qi) : (pi > 0.0) && (u < 1.0);
+        if (lane == 0) {
+          if (p.out_p) p.out_p[b * gamma + i] = float(pi);
+          if (p.out_q) p.out_q[b * gamma + i] = float(qi);
+        }
+        state = accept ? 0 : 1;
+      }
+      if (lane == 0) sh.state = state;
+    }
+    __syncthreads();
+    const int state = sh.state;
+    if (state == 2) {
+      if (wave == 0) write_fallback(p, b, SV_ROW_NONFINITE, lane);
+      return;
+    }
+    if (state == 1) {
+      k = i;
+      break;
+    }
+  }
+
+  SeqDecision dec;
+  if (k < gamma) {
+    // Residual masses over the two rows still in LDS.
+    const int jt = k, jd = gamma + 1 + k;
+    for (int64_t c = wave; c < nchunk; c += kFusedWaves) {
+      const int nvalid = chunk_valid(V, c);
+      RawChunk<T, VW> rt, rd;
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jt, V) + c * kChunk, nvalid, lane, rt);
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jd, V) + c * kChunk, nvalid, lane, rd);
+      const double w_c = residual_chunk_mass<T, VW>(rt, rd, nvalid, lane, prt[c],
+                                                    prt[nchunk + c], sh.st2[0], sh.st2[1], Td, kk);
+      if (lane == 0) wr[c] = w_c;
+    }
+    __syncthreads();
+    dec = SeqDecision{k, kDrawResidual, 0, 0};
+  } else {
+    sweep_pair<T, VW>(p, b, gamma, gamma, 1, prt, kk, wave, lane);
+    __syncthreads();
+    if (wave == 0) {
+      const RowStat st = merge_row(prt, nchunk, lane, Td);
+      if (lane == 0) sh.st2[0] = st;
+    }
+    __syncthreads();
+    if (!sh.st2[0].valid) {
+      if (wave == 0) write_fallback(p, b, SV_ROW_NONFINITE, lane);
+      return;
+    }
+    dec = SeqDecision{gamma, kDrawBonus, 0, 0};
+  }
+  if (wave != 0) return;
+  // The accepted prefix, padding, and positions after the cut (never evaluated: p, q NaN).
+  for (int i = lane; i <= gamma; i += kWave)
+    if (i != k) p.out_tokens[b * (gamma + 1) + i] = i < k ? g.x : -1;
+  for (int i = lane; i < gamma; i += kWave) {
+    if (i > k && p.out_p) p.out_p[b * gamma + i] = NAN;
+    if (i > k && p.out_q) p.out_q[b * gamma + i] = NAN;
+  }
+  draw_sequence<T, VW>(p, b, dec, PairSrc{sh.st2, prt, wr, nchunk, gamma});
+}
+
 // ------------------------------------------------------------------------------------ alpha
 
 // Acceptance rate alpha_i = sum_x min(p_i(x), q_i(x)) of position i of sequence b (the Step 3
@@ -1059,6 +1254,26 @@ constexpr int kChipFillMin = 192, kChipFillMax = 256;  // fused whatever the row
 constexpr int64_t kFinishMaxResidualBytes = 256 * 1024;
 constexpr int kFinishMaxBatch = 512;
 
+// Early exit (sv_verify_chain_lazy): the position-order kernel pays once the sequences give most
+// CUs a workgroup (measured: B = 256, gamma = 7, V = 152064 fp32: 224 vs 390 us; B = 1024, V =
+// 32000 bf16: 119 vs 132-153 us; B = 64, V = 128256 bf16: 102 vs 49 us).  Smaller batches take
+// the eager paths, whose outputs agree wherever the early-exit contract fixes them.
+// SPECVERIFY_CHAIN_PATH=lazy forces it (testing).
+constexpr int kLazyMinBatch = 128;
+
+inline size_t lazy_lds_bytes(int64_t nchunk) {
+  return (2 * sizeof(RowPart) + sizeof(double)) * size_t(nchunk);
+}
+
+inline bool use_lazy(const ChainArgs& a, int64_t nchunk) {
+  if (lazy_lds_bytes(nchunk) > kFusedMaxLds) return false;
+  const char* e = getenv("SPECVERIFY_CHAIN_PATH");
+  if (e && strcmp(e, "lazy") == 0) return true;
+  if (e && (strcmp(e, "fused") == 0 || strcmp(e, "finish") == 0 || strcmp(e, "split") == 0))
+    return false;
+  return a.B >= kLazyMinBatch;
+}
+
 inline size_t fused_lds_bytes(int gamma, int64_t nchunk) {
   return sizeof(RowPart) * size_t(2 * gamma + 1) * size_t(nchunk) + sizeof(double) * size_t(nchunk);
 }
@@ -1106,6 +1321,9 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   const ChainPath path =
       VW > 1 ? choose_path(a, L.nchunk, sizeof(T), with_rates) : ChainPath::kSplit;
   if constexpr (VW > 1) {
+    if (a.lazy && use_lazy(a, L.nchunk))
+      return launch_kernel_shm("chain_lazy", k_chain_lazy<T, VW>, dim3(unsigned(a.B)),
+                               dim3(kFusedBlock), lazy_lds_bytes(L.nchunk), s, p);
     if (path == ChainPath::kFused)
       return launch_kernel_shm("chain_fused", k_chain_fused<T, VW>, dim3(unsigned(a.B)),
                                dim3(kFusedBlock), fused_lds_bytes(a.gamma, L.nchunk), s, p);

@@ -214,7 +214,8 @@ struct ChainArgs {
   int32_t* out_status;
   float* out_alpha;  // [B, gamma] acceptance rates, or NULL (plain verification)
   char* ws;
-  bool vec;  // 16-byte vector-load path is legal
+  bool vec;   // 16-byte vector-load path is legal
+  bool lazy;  // early exit allowed: rows after the cut need not be read
 };
 
 struct TreeArgs {

@@ -70,10 +70,12 @@ def allowed_outcomes(target, draft, toks, uni, temp, res):
     return allowed, kind
 
 
-def check_chain(batch, out, seqs=None):
+def check_chain(batch, out, seqs=None, lazy=False):
     """Compare GPU chain outputs (numpy arrays) with the oracle on the listed sequences.
 
     out: dict with tokens [B, gamma+1], num_accepted [B], p, q [B, gamma], status [B].
+    lazy: outputs of the early-exit entry point, whose p and q after the cut k are either NaN
+    (row not read) or the evaluated values; positions i <= k are checked as usual.
     Returns counts {"exact": n, "accept_band": n, "edge_band": n, "fallback": n}.
     Raises AssertionError with a description on the first mismatch.
     """
@@ -97,6 +99,12 @@ def check_chain(batch, out, seqs=None):
         # probabilities
         for name, ref in (("p", res["p_at"]), ("q", res["q_at"])):
             got = np.asarray(out[name][b], dtype=np.float64)
+            if lazy:
+                tail = slice(k + 1, None)
+                assert np.all(np.isnan(got[tail]) | (np.abs(got[tail] - ref[tail])
+                                                     <= P_RTOL * np.abs(ref[tail]) + P_ATOL)), \
+                    f"seq {b}: {name} after the cut {got[tail]} oracle {ref[tail]}"
+                got, ref = got[:k + 1], ref[:k + 1]
             err = np.abs(got - ref)
             lim = P_RTOL * np.abs(ref) + P_ATOL
             bad = np.flatnonzero(~(err <= lim))

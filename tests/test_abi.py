@@ -67,12 +67,15 @@ def test_workspace_sizes():
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 
 
-def chain_call(**kw):
+CHAIN_ENTRIES = ["sv_verify_chain", "sv_verify_chain_lazy"]  # same signature and rules
+
+
+def chain_call(entry="sv_verify_chain", **kw):
     a = dict(target=FAKE, draft=FAKE, dtype=BD.SV_F32, toks=FAKE, uni=FAKE, temp=FAKE, B=1,
              gamma=4, V=1000, out_tokens=FAKE, out_nacc=FAKE, out_p=None, out_q=None,
              out_status=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
     a.update(kw)
-    return BD.load().sv_verify_chain(*a.values())
+    return getattr(BD.load(), entry)(*a.values())
 
 
 def tree_call(**kw):
@@ -83,10 +86,11 @@ def tree_call(**kw):
     return BD.load().sv_verify_tree(*a.values())
 
 
+@pytest.mark.parametrize("entry", CHAIN_ENTRIES)
 @pytest.mark.parametrize("field", ["target", "draft", "toks", "uni", "temp", "out_tokens",
                                    "out_nacc"])
-def test_chain_null_pointers(field):
-    assert chain_call(**{field: None}) == BD.SV_ERR_NULL
+def test_chain_null_pointers(field, entry):
+    assert chain_call(entry, **{field: None}) == BD.SV_ERR_NULL
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -97,8 +101,9 @@ def test_chain_null_pointers(field):
     (dict(ws=None), BD.SV_ERR_WORKSPACE), (dict(ws_bytes=16), BD.SV_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x1010)), BD.SV_ERR_WORKSPACE),
 ])
-def test_chain_validation(kw, status):
-    assert chain_call(**kw) == status
+@pytest.mark.parametrize("entry", CHAIN_ENTRIES)
+def test_chain_validation(kw, status, entry):
+    assert chain_call(entry, **kw) == status
 
 
 def rates_call(**kw):
@@ -122,6 +127,12 @@ def test_chain_with_rates_null_pointers(field):
 ])
 def test_chain_with_rates_validation(kw, status):
     assert rates_call(**kw) == status
+
+
+def test_early_exit_has_no_rates():
+    # The binding refuses the combination before it looks at any tensor.
+    with pytest.raises(ValueError):
+        BD.sv_verify_chain(None, None, None, None, None, lazy=True, want_rates=True)
 
 
 def test_chain_with_rates_needs_its_own_workspace_size():

@@ -54,10 +54,14 @@ def _same(a, b):
         assert np.array_equal(a[k], b[k], equal_nan=np.issubdtype(a[k].dtype, np.floating)), k
 
 
-@pytest.mark.parametrize("dtype,B,gamma,V,rates", [("bf16", 4, 4, 5000, False),
-                                                   ("f32", 3, 6, 4100, False),
-                                                   ("bf16", 3, 5, 6000, True)])
-def test_graph_chain(dtype, B, gamma, V, rates):
+@pytest.mark.parametrize("dtype,B,gamma,V,mode", [("bf16", 4, 4, 5000, "plain"),
+                                                  ("f32", 3, 6, 4100, "plain"),
+                                                  ("bf16", 3, 5, 6000, "rates"),
+                                                  ("f32", 5, 6, 4100, "lazy")])
+def test_graph_chain(dtype, B, gamma, V, mode, monkeypatch):
+    rates, lazy = mode == "rates", mode == "lazy"
+    if lazy:  # the early-exit kernel at this small batch
+        monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", "lazy")
     dev = torch.device("cuda:0")
     gen = lambda seed: I.chain_gaussian(seed, B, gamma, V, dtype, 2.0, 1.0, 0.8)
     d = BD.chain_to_device(gen(100), dev)
@@ -77,7 +81,7 @@ def test_graph_chain(dtype, B, gamma, V, rates):
                            d["temperature"], out_tokens=outs["tokens"],
                            out_num_accepted=outs["num_accepted"], out_p=outs["p"],
                            out_q=outs["q"], out_status=outs["status"],
-                           out_alpha=outs.get("alpha"), workspace_buf=ws)
+                           out_alpha=outs.get("alpha"), workspace_buf=ws, lazy=lazy)
 
     g = _capture(call)
     for seed in REPLAY_SEEDS:
@@ -87,10 +91,11 @@ def test_graph_chain(dtype, B, gamma, V, rates):
         torch.cuda.synchronize()
         got = _host(outs)
         eager = _host(BD.sv_verify_chain(d["target"], d["draft"], d["draft_tokens"],
-                                         d["uniforms"], d["temperature"], want_rates=rates))
+                                         d["uniforms"], d["temperature"], want_rates=rates,
+                                         lazy=lazy))
         torch.cuda.synchronize()
         _same(got, eager)
-        check_chain(batch, got)
+        check_chain(batch, got, lazy=lazy)
         if rates:
             check_acceptance_rates(batch, {"alpha": got["alpha"]})
 
