@@ -132,10 +132,11 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
  * out_p / out_q at positions i <= k; after the cut they are NaN where the row was not read and
  * sv_verify_chain's values elsewhere.
  * Rows after the cut may not be read: a non-finite value there may or may not set
- * SV_ROW_NONFINITE and the fallback.  Batches of at least 128 sequences take positions in order
- * in one launch, one workgroup per sequence, reading target and draft row i only while
- * position i is reached (and target row gamma only if every draft is accepted); smaller batches
- * run as sv_verify_chain.
+ * SV_ROW_NONFINITE and the fallback.  Batches of at least 128 sequences take the positions in
+ * order, reading target and draft row i only once position i is reached (and target row gamma
+ * only if every draft is accepted): with rows of 128 KiB or more, one launch per position across
+ * the whole chip (gamma + 2 launches, then the residual and draw kernels); with narrower rows,
+ * one launch with one workgroup per sequence.  Smaller batches run as sv_verify_chain.
  * ---------------------------------------------------------------------------------------- */
 sv_status sv_verify_chain_lazy(const void* target_logits, const void* draft_logits,
                                sv_dtype dtype, const int32_t* draft_tokens, const float* uniforms,

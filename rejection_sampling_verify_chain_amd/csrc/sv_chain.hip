@@ -66,6 +66,12 @@ struct ChainParams {
   float* out_p;
   float* out_q;
   int32_t* out_status;
+  // Staged early exit only: per sequence, "reached position j" flags [B][2] (slot j & 1), the
+  // checks that need no logit row [B], and the drafted tokens' target and draft logits
+  // [B][gamma][2].
+  int32_t* alive = nullptr;
+  int32_t* hstat = nullptr;
+  float* lz = nullptr;
 };
 
 template <typename T>
@@ -955,6 +961,181 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_lazy(ChainParams p) {
   draw_sequence<T, VW>(p, b, dec, PairSrc{sh.st2, prt, wr, nchunk, gamma});
 }
 
+// ------------------------------------------------------------------------ early exit, staged
+//
+// The positions in order with the whole chip on each: launch j (0 <= j <= gamma + 1) works on
+// every sequence that reached position j - 1, in workgroups that each take a slice of its
+// chunks.  Every workgroup first decides position j - 1 itself (waves 0 and 1 merge the chunk
+// partials of target and draft row j - 1; at j = gamma + 1 only target row gamma, the bonus
+// row), and workgroup 0 writes the sequence's outputs and, at a cut or the bonus row, the
+// decision and row statistics.  After an accept the workgroup sweeps its slice of row pair j
+// (target row gamma alone at j = gamma) into chunk partials and fetches the drafted token's two
+// logits at position j; otherwise it exits.  Launch 0 sweeps pair 0 of every sequence and checks
+// the inputs that need no logit row.  The multi-kernel path's residual and draw kernels then
+// finish every sequence from the decisions.  Rows after the cut are never read, and each step
+// calls the eager path's device functions on the same values, so the outputs agree with
+// sv_verify_chain bit for bit (p and q after the cut excepted).
+
+enum StageRole : int32_t { kStageExit = 0, kStageSweep = 1 };
+
+constexpr int kStageBlock = 256;
+constexpr int kStageWavesPerSimd = 8;
+template <typename T>
+constexpr int kStageUnits = (kStageBlock / kWave) * kUnitsPerWave<T>;  // chunks per workgroup
+
+// Workgroups per sequence in launch j: enough for the largest slice work of that launch.
+inline int stage_groups(int j, int gamma, int64_t nchunk, int units_per_group) {
+  if (j > gamma) return 1;
+  const int64_t units = (j < gamma ? 2 : 1) * nchunk;
+  return int((units + units_per_group - 1) / units_per_group);
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kStageBlock, kStageWavesPerSimd) void k_chain_stage(
+    ChainParams p, int j, int G) {
+  __shared__ RowStat st2[2];
+  __shared__ int32_t role;
+  const int64_t b = blockIdx.x / G;
+  const int g = int(blockIdx.x - b * G);
+  const bool lead = g == 0;  // writes the sequence's outputs
+  const int gamma = p.gamma;
+  const int R = 2 * gamma + 1;
+  const int64_t nchunk = p.nchunk;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & (kWave - 1);
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const float tb = uniform_load(p.temp, b);
+  const float te = effective_temperature(tb);
+  const double Td = te;
+  const float kk = log2e_over_t(te);
+
+  int r = kStageSweep;
+  if (j == 0) {
+    if (lead && wave == 0) {
+      // Checks that read no logit row; launch 1 takes the fallback on them.
+      int status = 0;
+      if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
+      bool bad = false;
+      for (int i = lane; i <= gamma; i += kWave) {
+        const float u = p.uni[b * (gamma + 1) + i];
+        bad |= !(u >= 0.0f && u < 1.0f);
+      }
+      if (__any(bad)) status |= SV_ROW_BAD_UNIFORM;
+      bad = false;
+      for (int i = lane; i < gamma; i += kWave) {
+        const int x = p.toks[b * gamma + i];
+        bad |= (x < 0) || (int64_t(x) >= p.V);
+      }
+      if (__any(bad)) status |= SV_ROW_TOKEN_RANGE;
+      if (lane == 0) {
+        p.hstat[b] = status;
+        p.alive[b * 2] = 1;
+      }
+    }
+  } else {
+    const int i = j - 1;  // the position decided here; i == gamma: the bonus row
+    if (!uniform_load(p.alive, b * 2 + (i & 1))) {
+      if (lead && threadIdx.x == 0) p.alive[b * 2 + (j & 1)] = 0;
+      return;  // the whole workgroup: the flag is uniform
+    }
+    if (wave < (i < gamma ? 2 : 1)) {
+      const RowStat st = merge_row(p.part + (b * R + (wave == 0 ? i : gamma + 1 + i)) * nchunk,
+                                   nchunk, lane, Td);
+      if (lane == 0) st2[wave] = st;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const RowStat a = st2[0];
+      const RowStat d = i < gamma ? st2[1] : a;
+      int status = i == 0 ? uniform_load(p.hstat, b) : 0;
+      if (!a.valid || !d.valid) status |= SV_ROW_NONFINITE;
+      int rr = kStageExit;
+      if (status != 0) {
+        if (lead) {
+          write_fallback(p, b, status, lane);
+          if (lane == 0) p.seq[b] = SeqDecision{0, kDrawNone, status, 0};
+        }
+      } else if (i == gamma) {
+        if (lead && lane == 0) {
+          p.rowstat[b * R + gamma] = a;
+          p.seq[b] = SeqDecision{gamma, kDrawBonus, 0, 0};
+        }
+      } else {
+        // Position i's test on the logits launch i fetched (the eager path's arithmetic).
+        const int x = uniform_load(p.toks, b * gamma + i);
+        const float zt = uniform_load(p.lz, (b * gamma + i) * 2);
+        const float zd = uniform_load(p.lz, (b * gamma + i) * 2 + 1);
+        const double pi = exp((double(zt) - double(a.m)) / Td) / a.s;
+        const double qi = exp((double(zd) - double(d.m)) / Td) / d.s;
+        const double u = uniform_load(p.uni, b * (gamma + 1) + i);
+        const bool accept = qi > 0.0 ? u < fmin(1.0, pi / qi) : (pi > 0.0) && (u < 1.0);
+        if (lead) {
+          if (lane == 0) {
+            if (p.out_p) p.out_p[b * gamma + i] = float(pi);
+            if (p.out_q) p.out_q[b * gamma + i] = float(qi);
+          }
+          if (accept) {
+            if (lane == 0) p.out_tokens[b * (gamma + 1) + i] = x;
+          } else {
+            // The cut: padding, and positions never evaluated (p, q NaN).
+            for (int t = i + 1 + lane; t <= gamma; t += kWave) {
+              p.out_tokens[b * (gamma + 1) + t] = -1;
+              if (t < gamma && p.out_p) p.out_p[b * gamma + t] = NAN;
+              if (t < gamma && p.out_q) p.out_q[b * gamma + t] = NAN;
+            }
+            if (lane == 0) {
+              p.rowstat[b * R + i] = a;
+              p.rowstat[b * R + gamma + 1 + i] = d;
+              p.seq[b] = SeqDecision{i, kDrawResidual, 0, 0};
+            }
+          }
+        }
+        rr = accept ? kStageSweep : kStageExit;
+      }
+      if (lead && lane == 0) p.alive[b * 2 + (j & 1)] = rr == kStageSweep ? 1 : 0;
+      if (lane == 0) role = rr;
+    }
+    __syncthreads();
+    r = role;
+  }
+
+  constexpr int U = kUnitsPerWave<T>;
+  const int64_t u0 = int64_t(g) * kStageUnits<T> + int64_t(wave) * U;
+  if (r == kStageSweep) {
+    if (lead && wave == 0 && j < gamma) {
+      // The drafted token's logits at position j, for launch j + 1's test.
+      const int x = uniform_load(p.toks, b * gamma + j);
+      if (lane == 0 && x >= 0 && int64_t(x) < p.V) {
+        p.lz[(b * gamma + j) * 2] = widen(chain_row(tgt, drf, b, gamma, j, p.V)[x]);
+        p.lz[(b * gamma + j) * 2 + 1] = widen(chain_row(tgt, drf, b, gamma, gamma + 1 + j, p.V)[x]);
+      }
+    }
+    const int64_t units = (j < gamma ? 2 : 1) * nchunk;
+    RawChunk<T, VW> raw[U];
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int64_t w = min(u0 + t, units - 1);
+      const int row = w < nchunk ? j : gamma + 1 + j;
+      const int64_t c = w < nchunk ? w : w - nchunk;
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, row, p.V) + c * kChunk, chunk_valid(p.V, c),
+                      lane, raw[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int64_t w = u0 + t;
+      if (w < units) {  // wave-uniform
+        const int row = w < nchunk ? j : gamma + 1 + j;
+        const int64_t c = w < nchunk ? w : w - nchunk;
+        float z[kElemsPerLane];
+        unpack_chunk<T, VW>(raw[t], chunk_valid(p.V, c), lane, z);
+        const RowPart rp = reduce_chunk(z, kk);
+        if (lane == 0) p.part[(b * R + row) * nchunk + c] = rp;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------ alpha
 
 // Acceptance rate alpha_i = sum_x min(p_i(x), q_i(x)) of position i of sequence b (the Step 3
@@ -1254,24 +1435,39 @@ constexpr int kChipFillMin = 192, kChipFillMax = 256;  // fused whatever the row
 constexpr int64_t kFinishMaxResidualBytes = 256 * 1024;
 constexpr int kFinishMaxBatch = 512;
 
-// Early exit (sv_verify_chain_lazy): the position-order kernel pays once the sequences give most
-// CUs a workgroup (measured: B = 256, gamma = 7, V = 152064 fp32: 224 vs 390 us; B = 1024, V =
-// 32000 bf16: 119 vs 132-153 us; B = 64, V = 128256 bf16: 102 vs 49 us).  Smaller batches take
-// the eager paths, whose outputs agree wherever the early-exit contract fixes them.
-// SPECVERIFY_CHAIN_PATH=lazy forces it (testing).
+// Early exit (sv_verify_chain_lazy) pays once the sequences give most CUs work; smaller batches
+// take the eager paths, whose outputs agree wherever the early-exit contract fixes them.  Of the
+// two forms, one launch per position (staged) pays for wide rows, whose pair of rows one CU would
+// read slowly, and one workgroup per sequence for narrow ones, where the launches' fixed cost
+// would dominate.  Measured per call (staged / one workgroup / eager): B = 256, gamma = 7,
+// V = 152064 fp32: 190 / 225 / 400 us; B = 128, same rows: 134 / 208 / 213 us; B = 1024,
+// gamma = 4, V = 32000 bf16: 115 / 118 / 151 us; B = 512, gamma = 7, V = 32000 bf16 with drafts
+// close to the target: 125 / 111 / 122 us; B = 64, gamma = 4, V = 128256 bf16: 66 / 102 / 48 us.
+// SPECVERIFY_CHAIN_PATH=lazy or staged forces a form (testing).
 constexpr int kLazyMinBatch = 128;
+constexpr int64_t kStagedMinPairBytes = 256 * 1024;
 
 inline size_t lazy_lds_bytes(int64_t nchunk) {
   return (2 * sizeof(RowPart) + sizeof(double)) * size_t(nchunk);
 }
 
-inline bool use_lazy(const ChainArgs& a, int64_t nchunk) {
-  if (lazy_lds_bytes(nchunk) > kFusedMaxLds) return false;
+enum class LazyForm { kNone, kOneGroup, kStaged };
+
+// The early-exit form sv_verify_chain_lazy takes (kNone: the eager paths).
+inline LazyForm lazy_form(const ChainArgs& a, int64_t nchunk, int units_per_group,
+                          size_t elem_bytes) {
+  const bool staged_ok =
+      int64_t(a.B) * stage_groups(0, a.gamma, nchunk, units_per_group) < int64_t(INT32_MAX);
+  const bool group_ok = lazy_lds_bytes(nchunk) <= kFusedMaxLds;
   const char* e = getenv("SPECVERIFY_CHAIN_PATH");
-  if (e && strcmp(e, "lazy") == 0) return true;
+  if (e && strcmp(e, "staged") == 0) return staged_ok ? LazyForm::kStaged : LazyForm::kNone;
+  if (e && strcmp(e, "lazy") == 0) return group_ok ? LazyForm::kOneGroup : LazyForm::kNone;
   if (e && (strcmp(e, "fused") == 0 || strcmp(e, "finish") == 0 || strcmp(e, "split") == 0))
-    return false;
-  return a.B >= kLazyMinBatch;
+    return LazyForm::kNone;
+  if (a.B < kLazyMinBatch) return LazyForm::kNone;
+  if (2 * a.V * int64_t(elem_bytes) >= kStagedMinPairBytes || !group_ok)
+    return staged_ok ? LazyForm::kStaged : LazyForm::kNone;
+  return LazyForm::kOneGroup;
 }
 
 inline size_t fused_lds_bytes(int gamma, int64_t nchunk) {
@@ -1316,12 +1512,34 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   p.out_p = a.out_p;
   p.out_q = a.out_q;
   p.out_status = a.out_status;
+  p.alive = reinterpret_cast<int32_t*>(a.ws + L.off_alive);
+  p.hstat = reinterpret_cast<int32_t*>(a.ws + L.off_hstat);
+  p.lz = reinterpret_cast<float*>(a.ws + L.off_lz);
 
   // The one-element-load forms of the one-workgroup kernel would spill; they take the split path.
   const ChainPath path =
       VW > 1 ? choose_path(a, L.nchunk, sizeof(T), with_rates) : ChainPath::kSplit;
   if constexpr (VW > 1) {
-    if (a.lazy && use_lazy(a, L.nchunk))
+    const LazyForm form =
+        a.lazy ? lazy_form(a, L.nchunk, kStageUnits<T>, sizeof(T)) : LazyForm::kNone;
+    if (form == LazyForm::kStaged) {
+      for (int j = 0; j <= a.gamma + 1; ++j) {
+        const int G = stage_groups(j, a.gamma, L.nchunk, kStageUnits<T>);
+        const hipError_t e = launch_kernel("chain_stage", k_chain_stage<T, VW>,
+                                           dim3(unsigned(int64_t(a.B) * G)),
+                                           dim3(kStageBlock), s, p, j, G);
+        if (e != hipSuccess) return e;
+      }
+      const int64_t rtotal = int64_t(a.B) * L.nchunk;
+      constexpr int rw = kResidualBlock / kWave;
+      const hipError_t e = launch_kernel("chain_residual", k_chain_residual<T, VW>,
+                                         dim3(unsigned((rtotal + rw - 1) / rw)),
+                                         dim3(kResidualBlock), s, p, rtotal);
+      if (e != hipSuccess) return e;
+      return launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s,
+                           p);
+    }
+    if (form == LazyForm::kOneGroup)
       return launch_kernel_shm("chain_lazy", k_chain_lazy<T, VW>, dim3(unsigned(a.B)),
                                dim3(kFusedBlock), lazy_lds_bytes(L.nchunk), s, p);
     if (path == ChainPath::kFused)

@@ -66,11 +66,13 @@ inline int64_t groups_per_unit(int64_t rows_per_unit, int64_t V) {
 }
 
 // Workspace: per (row, chunk) partials, per row statistics, per sequence decisions, per
-// (sequence, chunk) residual masses.  Every entry is written before it is read within a call.
+// (sequence, chunk) residual masses, and the staged early exit's per-sequence flags and drafted
+// logits.  Every entry is written before it is read within a call.
 // with_rates: also the per (sequence, position, chunk) overlap sums of the acceptance rates.
 struct ChainLayout {
   int64_t nchunk;
-  size_t off_part, off_rowstat, off_seq, off_wres, off_alpha_sum, total;
+  size_t off_part, off_rowstat, off_seq, off_wres, off_alive, off_hstat, off_lz, off_alpha_sum,
+      total;
 };
 
 inline ChainLayout chain_layout(int64_t B, int64_t gamma, int64_t V, bool with_rates = false) {
@@ -86,6 +88,12 @@ inline ChainLayout chain_layout(int64_t B, int64_t gamma, int64_t V, bool with_r
   off += align256(sizeof(SeqDecision) * size_t(B));
   L.off_wres = off;
   off += align256(sizeof(double) * size_t(B) * size_t(L.nchunk));
+  L.off_alive = off;  // staged early exit: [B][2] int32
+  off += align256(sizeof(int32_t) * 2 * size_t(B));
+  L.off_hstat = off;  // [B] int32
+  off += align256(sizeof(int32_t) * size_t(B));
+  L.off_lz = off;  // [B][gamma][2] fp32
+  off += align256(sizeof(float) * 2 * size_t(B) * size_t(gamma));
   L.off_alpha_sum = off;
   if (with_rates) off += align256(sizeof(double) * size_t(B) * size_t(gamma) * size_t(L.nchunk));
   L.total = off;

@@ -57,11 +57,12 @@ def _same(a, b):
 @pytest.mark.parametrize("dtype,B,gamma,V,mode", [("bf16", 4, 4, 5000, "plain"),
                                                   ("f32", 3, 6, 4100, "plain"),
                                                   ("bf16", 3, 5, 6000, "rates"),
-                                                  ("f32", 5, 6, 4100, "lazy")])
+                                                  ("f32", 5, 6, 4100, "lazy"),
+                                                  ("bf16", 4, 5, 6000, "staged")])
 def test_graph_chain(dtype, B, gamma, V, mode, monkeypatch):
-    rates, lazy = mode == "rates", mode == "lazy"
-    if lazy:  # the early-exit kernel at this small batch
-        monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", "lazy")
+    rates, lazy = mode == "rates", mode in ("lazy", "staged")
+    if lazy:  # an early-exit form at this small batch
+        monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", mode)
     dev = torch.device("cuda:0")
     gen = lambda seed: I.chain_gaussian(seed, B, gamma, V, dtype, 2.0, 1.0, 0.8)
     d = BD.chain_to_device(gen(100), dev)

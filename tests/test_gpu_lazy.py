@@ -3,8 +3,9 @@
 The early-exit entry point takes the positions in order and reads no row after the cut.  For
 inputs whose rows are all finite its tokens, k and status must be sv_verify_chain's bit for bit
 and its p, q at positions i <= k too; after the cut p and q are NaN where the row was not read.
-Most tests force the early-exit kernel (SPECVERIFY_CHAIN_PATH=lazy), which the library otherwise
-takes from 128 sequences on; the threshold and full-size tests leave the choice to the library.
+Most tests force each of the two early-exit forms (SPECVERIFY_CHAIN_PATH=lazy: one workgroup per
+sequence; staged: one launch per position), whatever the batch; the threshold and full-size tests
+leave the choice to the library.
 """
 
 import numpy as np
@@ -18,9 +19,12 @@ from rejection_sampling_verify_chain_amd import inputs as I
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture
-def forced(monkeypatch):
-    monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", "lazy")
+@pytest.fixture(params=["lazy", "staged"])
+def forced(request, monkeypatch):
+    """Both early-exit forms: one workgroup per sequence taking the positions in order, and one
+    launch per position across the chip."""
+    monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", request.param)
+    return request.param
 
 
 def run(batch, lazy=True, d=None):

@@ -4,7 +4,7 @@ Each case draws its shape (batch, gamma, vocabulary, node count, row width), dty
 and logit scales from a fixed seed, builds the inputs with the seeded generators, and compares
 the library's outputs with the oracle by the same rules as the other parity tests.  The shapes
 cross the chunk (2048) and vector-width boundaries at random, including V = 1 and gamma = 1;
-chain cases run on all three chain paths and on the early-exit kernel.
+chain cases run on all three chain paths and on both early-exit forms.
 """
 
 import numpy as np
@@ -34,7 +34,7 @@ def _host(out):
     return {k: (None if v is None else v.cpu().numpy()) for k, v in out.items()}
 
 
-@pytest.mark.parametrize("path", ["fused", "finish", "split", "lazy"])
+@pytest.mark.parametrize("path", ["fused", "finish", "split", "lazy", "staged"])
 @pytest.mark.parametrize("case", CASES)
 def test_random_chain(case, path, monkeypatch):
     rng = _rng(1, case)
@@ -45,7 +45,7 @@ def test_random_chain(case, path, monkeypatch):
                          float(rng.uniform(0.1, 2.0)), T, draft_scale=float(rng.uniform(0.5, 1.0)))
     monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", path)
     d = BD.chain_to_device(b)
-    lazy = path == "lazy"  # the early-exit entry point, forced onto its kernel
+    lazy = path in ("lazy", "staged")  # the early-exit entry point, forced onto either form
     check_chain(b, _host(BD.sv_verify_chain(d["target"], d["draft"], d["draft_tokens"],
                                             d["uniforms"], d["temperature"], lazy=lazy)),
                 lazy=lazy)
