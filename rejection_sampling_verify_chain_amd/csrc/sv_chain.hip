@@ -655,7 +655,7 @@ __global__ __launch_bounds__(kWave) void k_chain_draw(ChainParams p) {
 constexpr int kFusedBlock = 1024;
 constexpr int kFusedWaves = kFusedBlock / kWave;
 template <typename T>
-constexpr int kFusedUnits = kUnitsPerWave<T>;  // chunks per wave in flight: 8 KiB
+constexpr int kFusedUnits = kUnitsPerWave<T>;  // chunks per wave in flight
 
 struct FusedShared {
   RowStat st[2 * kMaxGamma + 1];
@@ -691,7 +691,7 @@ __device__ __forceinline__ void one_workgroup_chain(const ChainParams& p, unsign
     for (int w = int(threadIdx.x); w < units; w += kFusedBlock) prt[w] = part[w];
   } else {
   // Sweep: the chunk partials of every row (virtual row j as in chain_row), kFusedUnits
-  // consecutive units per wave with all their loads in flight (8 KiB of logits; more spills at
+  // consecutive units per wave with all their loads in flight (two fp32 chunks per wave spill at
   // the 128 registers a 1024-thread workgroup allows); a unit past the end reloads the last one
   // and is not reduced.
   constexpr int U = kFusedUnits<T>;
@@ -775,6 +775,11 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_finish(ChainParams p) {
 // functions as the other paths, so for inputs whose rows are all finite the outputs are theirs
 // bit for bit; only non-finite values in unread rows go unseen.
 
+// Chunks per wave in flight when one workgroup sweeps a row pair: 8 KiB of logits (two bf16
+// chunks measured 2-3% faster here than one, unlike the chip-wide sweeps).
+template <typename T>
+constexpr int kLazyUnits = 4 / int(sizeof(T));
+
 // The draw's records for the row pair in LDS: slot 0 holds target row j <= gamma, slot 1 draft row
 // j > gamma.
 struct PairSrc {
@@ -803,7 +808,7 @@ __device__ __forceinline__ void sweep_pair(const ChainParams& p, int64_t b, int 
   const T* tgt = static_cast<const T*>(p.tgt);
   const T* drf = static_cast<const T*>(p.drf);
   const int nchunk = int(p.nchunk);
-  constexpr int U = kFusedUnits<T>;
+  constexpr int U = kLazyUnits<T>;
   const int units = nrows * nchunk;
   for (int w0 = wave * U; w0 < units; w0 += kFusedWaves * U) {
     RawChunk<T, VW> r[U];

@@ -143,17 +143,17 @@ __device__ __forceinline__ void unpack_chunk(const RawChunk<T, VW>& r, int nvali
 
 // ---------------------------------------------------------------------------- streaming waves
 //
-// The streaming kernels (softmax partials, argmax partials) give each wave 8 KiB of logits to
-// load at once: one fp32 chunk or two consecutive bf16 chunks, both loads issued before either
-// is reduced.  Units are the chunks of all rows in row-major order, unit w = row * nchunk + c
-// (a row's last chunk may be partial), rows coming in groups of R (the rows of one sequence).
-// Measured alternatives that lost: a persistent grid-stride loop with the next unit's loads in
-// flight (slower at every size here), and moving the partial chunks into waves of their own
-// (2% slower on a 2.3 GB fp32 sweep).
+// The streaming kernels (softmax partials, argmax partials) give each wave one chunk of logits
+// to load at once (8 KiB of fp32, 4 KiB of bf16), all its loads issued before it is reduced.
+// Units are the chunks of all rows in row-major order, unit w = row * nchunk + c (a row's last
+// chunk may be partial), rows coming in groups of R (the rows of one sequence).  Measured
+// alternatives that lost: a persistent grid-stride loop with the next unit's loads in flight
+// (slower at every size here), moving the partial chunks into waves of their own (2% slower on
+// a 2.3 GB fp32 sweep), and two bf16 chunks per wave (6-7% slower on the 148 MB bf16 sweeps).
 
-// Units a wave takes: 8 KiB of logits in flight per wave.
+// Units (chunks) a wave takes.
 template <typename T>
-constexpr int kUnitsPerWave = 4 / int(sizeof(T));
+constexpr int kUnitsPerWave = 1;
 
 // Workgroup size of the streaming kernels (measured): 1024 threads for fp32 logits, 256 for bf16.
 template <typename T>
