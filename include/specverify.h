@@ -349,6 +349,21 @@ int sv_trace_kernels(void);
 int sv_trace_get(int index, char* name, size_t name_len, int* launches, double* total_ms,
                  double* min_ms, double* max_ms);
 
+/* ------------------------------------------------------------------------------------------
+ * Streaming-read ceiling (measurement support; not part of the verify step).
+ *
+ * sv_read_probe(src, bytes, out, stream): reads the `bytes` bytes at device address src once,
+ *   the way the streaming kernels read logits (one 8 KiB piece per wave as 16-byte nontemporal
+ *   loads, 1024-thread workgroups), and writes the XOR of the 32-bit words each workgroup read to
+ *   out (device, uint32 [sv_read_probe_out_words(bytes)], caller-owned), so that no load is
+ *   dropped.  Its kernel time (traced as "read_probe") is the rate of a plain read of that size.
+ *   Returns SV_ERR_NULL for a NULL pointer, SV_ERR_SHAPE when bytes is not a positive multiple
+ *   of 16 or src is not 16-byte aligned, SV_ERR_LAUNCH if the launch fails, else SV_OK.
+ * sv_read_probe_out_words(bytes): output words for that size (0 when the size is invalid).
+ * ---------------------------------------------------------------------------------------- */
+size_t sv_read_probe_out_words(int64_t bytes);
+sv_status sv_read_probe(const void* src, int64_t bytes, uint32_t* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,7 @@ EXPORTS = (
     "sv_sample_workspace_bytes", "sv_sample",
     "sv_compact_accepted",
     "sv_trace_start", "sv_trace_stop", "sv_trace_kernels", "sv_trace_get",
+    "sv_read_probe_out_words", "sv_read_probe",
 )
 
 _DTYPE = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}
@@ -106,6 +107,11 @@ def load():
     lib.sv_trace_get.argtypes = [ctypes.c_int, ctypes.c_char_p, sz, ctypes.POINTER(ctypes.c_int),
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_double)]
+    lib.sv_read_probe_out_words.restype = sz
+    lib.sv_read_probe_out_words.argtypes = [ctypes.c_int64]
+    lib.sv_read_probe.restype = ctypes.c_int
+    lib.sv_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -394,6 +400,27 @@ def sv_sample(logits, temperature, uniforms, *, out_tokens=None, out_prob=None, 
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_sample")
     return {"tokens": out_tokens, "prob": out_prob, "status": out_status}
+
+
+def read_probe_out_words(nbytes):
+    return int(load().sv_read_probe_out_words(int(nbytes)))
+
+
+def sv_read_probe(buf, *, out=None, stream=None):
+    """Plain streaming read of a contiguous device tensor (the read ceiling the verify kernels
+    are set beside); returns the int32 tensor of per-workgroup XORs of the words read."""
+    lib = load()
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    words = read_probe_out_words(nbytes)
+    if words == 0:
+        raise ValueError(f"buf size {nbytes} is not a positive multiple of 16 bytes")
+    out = _out(out, "out", torch.int32, (words,), buf.device)
+    st = lib.sv_read_probe(_ptr(buf), nbytes, _ptr(out), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_read_probe")
+    return out
 
 
 def sv_compact_accepted(src, dst, num_accepted, dst_start, path=None, *, out_status=None,

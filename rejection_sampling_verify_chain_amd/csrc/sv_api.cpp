@@ -329,3 +329,18 @@ SV_EXPORT sv_status sv_compact_accepted(const void* src, void* dst, int64_t row_
   a.out_status = out_status;
   return sv::launch_kv_compact(a, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
+
+// ---------------------------------------------------------------------- measurement support
+
+SV_EXPORT size_t sv_read_probe_out_words(int64_t bytes) {
+  if (bytes <= 0 || bytes % 16 != 0) return 0;
+  const int64_t g = sv::read_probe_groups(bytes);
+  return g < int64_t(INT32_MAX) ? size_t(g) : 0;
+}
+
+SV_EXPORT sv_status sv_read_probe(const void* src, int64_t bytes, uint32_t* out,
+                                  hipStream_t stream) {
+  if (!src || !out) return SV_ERR_NULL;
+  if (sv_read_probe_out_words(bytes) == 0 || !aligned16(src)) return SV_ERR_SHAPE;
+  return sv::launch_read_probe(src, bytes, out, stream) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}

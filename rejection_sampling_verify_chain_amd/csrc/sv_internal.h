@@ -264,4 +264,9 @@ hipError_t launch_alpha(const AlphaArgs& a, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 hipError_t launch_kv_compact(const KvArgs& a, hipStream_t stream);
 
+// Streaming-read ceiling (measurement support): workgroups the probe launches for `bytes`, and
+// the launch (one output word per workgroup).
+int64_t read_probe_groups(int64_t bytes);
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, hipStream_t s);
+
 }  // namespace sv

@@ -238,3 +238,18 @@ def test_kv_null_pointers(field):
                                 dict(dst=ctypes.c_void_p(0x100000 + 4096))])  # overlaps src
 def test_kv_host_validation(kw):
     assert kv_call(**kw) == BD.SV_ERR_SHAPE
+
+
+def test_read_probe_sizes_and_validation():
+    lib = BD.load()
+    group = 128 * 1024  # bytes one probe workgroup reads
+    assert lib.sv_read_probe_out_words(16) == 1
+    assert lib.sv_read_probe_out_words(group) == 1
+    assert lib.sv_read_probe_out_words(group + 16) == 2
+    assert lib.sv_read_probe_out_words(0) == 0 and lib.sv_read_probe_out_words(24) == 0
+    assert lib.sv_read_probe_out_words(-16) == 0
+    # Every call below fails validation before any launch.
+    assert lib.sv_read_probe(None, 16, FAKE, None) == BD.SV_ERR_NULL
+    assert lib.sv_read_probe(FAKE, 16, None, None) == BD.SV_ERR_NULL
+    assert lib.sv_read_probe(FAKE, 24, FAKE, None) == BD.SV_ERR_SHAPE
+    assert lib.sv_read_probe(ctypes.c_void_p(0x1008), 16, FAKE, None) == BD.SV_ERR_SHAPE
