@@ -8,9 +8,13 @@
 // norm(max(0, p - q)), and the expected-speedup section the (gamma+1)-th token
 // of a fully accepted round.
 //
-// Sequences with small rows (up to 256 KiB of logits, at most 256 sequences) take a single
-// launch, chain_fused, one workgroup per sequence (its section below).  Otherwise four
-// launches per call, all on the caller's stream, no host synchronisation:
+// sv_verify_chain takes one of three paths, chosen by measured thresholds (choose_path), all
+// with the same bits: a single launch with one workgroup per sequence (chain_fused, for small
+// rows or 192..256 sequences), the sweep followed by one workgroup per sequence (chain_finish),
+// or the four launches below.  sv_verify_chain_lazy takes the positions in order and reads no
+// row after the cut (lazy_form): one launch per position across the chip (chain_stage), or one
+// workgroup per sequence (chain_lazy).  All launches go on the caller's stream, with no host
+// synchronisation.  The four launches of the split path:
 //   sweep     the single HBM sweep over all B*(2*gamma+1)*V logits: each wave owns one chunk
 //             (2048 elements) of one logit row and writes its chunk max m_c and
 //             S_c = sum exp((z - m_c)/T) (fp32 terms, fp64 sum).
