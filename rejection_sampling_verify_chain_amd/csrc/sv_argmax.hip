@@ -23,8 +23,7 @@ namespace {
 // row's last chunk a hit at or past nvalid means none in range.  A chunk of only NaN has m =
 // NaN and no hit.
 template <int VW, bool TAIL>
-__device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane], int nvalid,
-                                                int lane) {
+__device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane], int nvalid) {
   constexpr int NLD = kElemsPerLane / VW;
   float mj[NLD];
   bool nan = false;
@@ -74,8 +73,8 @@ __global__ __launch_bounds__(kStreamBlock<T>, kStreamWavesPerSimd<VW>) void k_ar
         const int nvalid = chunk_valid(V, k.c);
         float z[kElemsPerLane];
         unpack_chunk<T, VW>(r, nvalid, lane, z);
-        ArgPart a = nvalid == kChunk ? argmax_chunk<VW, false>(z, nvalid, lane)
-                                     : argmax_chunk<VW, true>(z, nvalid, lane);
+        ArgPart a = nvalid == kChunk ? argmax_chunk<VW, false>(z, nvalid)
+                                     : argmax_chunk<VW, true>(z, nvalid);
         a.idx = a.idx == INT32_MAX ? INT32_MAX : a.idx + k.c * kChunk;
         if (lane == 0) part[k.w] = a;
       });
