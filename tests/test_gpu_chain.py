@@ -154,6 +154,22 @@ def test_deterministic():
         assert np.array_equal(o1[k], o2[k]), k
 
 
+def test_same_bits_on_another_stream():
+    # No float atomics and no cross-call state: a call on a side stream gives the same bits.
+    b = I.chain_gaussian(17, 6, 5, 5003, "bf16", 2.0, 1.0, 0.9)
+    d = BD.chain_to_device(b)
+    args = (d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["temperature"])
+    ref = BD.sv_verify_chain(*args)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = BD.sv_verify_chain(*args, stream=side)
+    side.synchronize()
+    for k in ref:
+        assert torch.equal(torch.nan_to_num(ref[k]), torch.nan_to_num(got[k])), k
+
+
 def _many(zt, zd, T, N, seed):
     """N sequences sharing the logits, with draft tokens drawn from q and fresh uniforms."""
     rng = np.random.default_rng(seed)

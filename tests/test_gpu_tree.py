@@ -132,3 +132,18 @@ def test_deterministic():
     o1, o2 = run_tree(b), run_tree(b)
     for k in o1:
         assert np.array_equal(o1[k], o2[k]), k
+
+
+def test_same_bits_on_another_stream():
+    b = I.tree_random(21, 5, 64, 5000, "bf16", boost=20.0, boost_prob=0.8)
+    d = BD.tree_to_device(b)
+    args = (d["logits"], d["parents"], d["node_tokens"])
+    ref = BD.sv_verify_tree(*args)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = BD.sv_verify_tree(*args, stream=side)
+    side.synchronize()
+    for k in ref:
+        assert torch.equal(ref[k], got[k]), k
