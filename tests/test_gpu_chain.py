@@ -231,3 +231,45 @@ def test_paths_bit_identical(dtype, B, gamma, V, T, monkeypatch):
     for k in outs["split"]:
         for path in ("fused", "finish"):
             assert np.array_equal(outs[path][k], outs["split"][k], equal_nan=True), (path, k)
+
+
+def test_concurrent_host_threads():
+    # The library keeps no per-call host state: calls from several host threads, each on its
+    # own stream, give the same bits as one call at a time.
+    import threading
+    batches = [I.chain_gaussian(40 + t, 5, 4, 3000 + 100 * t, "f32", 2.0, 1.0, 1.0)
+               for t in range(4)]
+    devs = [BD.chain_to_device(b) for b in batches]
+    refs = []
+    for d in devs:
+        refs.append(BD.sv_verify_chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"],
+                                       d["temperature"]))
+    torch.cuda.synchronize()
+    got = [None] * len(devs)
+    errors = []
+
+    def work(t):
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.default_stream())
+            d = devs[t]
+            # Outputs and workspace are allocated on the thread's stream too, so the caching
+            # allocator hands a freed block only to later work on that same stream.
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    o = BD.sv_verify_chain(d["target"], d["draft"], d["draft_tokens"],
+                                           d["uniforms"], d["temperature"], stream=s)
+            s.synchronize()
+            got[t] = o
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(len(devs))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for ref, o in zip(refs, got):
+        for k in ref:
+            assert torch.equal(torch.nan_to_num(ref[k]), torch.nan_to_num(o[k])), k
