@@ -137,6 +137,9 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
  * only if every draft is accepted): with rows of 128 KiB or more, one launch per position across
  * the whole chip (gamma + 2 launches, then the residual and draw kernels); with narrower rows,
  * one launch with one workgroup per sequence.  Smaller batches run as sv_verify_chain.
+ * SPECVERIFY_CHAIN_PATH=staged or =lazy, read on every call, forces the one-launch-per-position
+ * form or the one-workgroup form at any batch size (testing and measurement; the one-workgroup
+ * form needs the row pair's partials to fit 32 KiB of LDS).
  * ---------------------------------------------------------------------------------------- */
 sv_status sv_verify_chain_lazy(const void* target_logits, const void* draft_logits,
                                sv_dtype dtype, const int32_t* draft_tokens, const float* uniforms,
