@@ -189,3 +189,25 @@ def test_deterministic(forced):
         for key in first:
             assert np.array_equal(first[key], again[key], equal_nan=True), key
 
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unaligned_rows_run_as_verify_chain(forced, dtype):
+    # Rows that are not 16-byte aligned have no early-exit form: the entry point runs
+    # sv_verify_chain (every p and q evaluated), forced or not.
+    b = I.chain_gaussian(18, 4, 3, 4096, dtype, 2.0, 1.0, 1.0)
+    d = BD.chain_to_device(b)
+
+    def shifted(t):
+        flat = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = flat[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    tgt, drf = shifted(d["target"]), shifted(d["draft"])
+    out = BD.sv_verify_chain(tgt, drf, d["draft_tokens"], d["uniforms"], d["temperature"],
+                             lazy=True)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in out.items()}
+    assert not np.isnan(out["p"]).any()
+    report(f"unaligned {dtype}", check_chain(b, out))
