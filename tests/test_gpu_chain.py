@@ -273,3 +273,18 @@ def test_concurrent_host_threads():
     for ref, o in zip(refs, got):
         for k in ref:
             assert torch.equal(torch.nan_to_num(ref[k]), torch.nan_to_num(o[k])), k
+
+
+def test_optional_outputs_omitted():
+    # out_p, out_q and out_status are optional: without them the tokens and counts are the same
+    # (every kernel that writes them checks for NULL), including fallback sequences.
+    b = I.chain_gaussian(19, 6, 5, 4100, "bf16", 2.0, 1.0, 0.8)
+    b.temperature[2] = -1.0
+    d = BD.chain_to_device(b)
+    args = (d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["temperature"])
+    full = BD.sv_verify_chain(*args)
+    bare = BD.sv_verify_chain(*args, want_pq=False, want_status=False)
+    torch.cuda.synchronize()
+    assert bare["p"] is None and bare["q"] is None and bare["status"] is None
+    for k in ("tokens", "num_accepted"):
+        assert torch.equal(full[k], bare[k]), k

@@ -211,3 +211,15 @@ def test_unaligned_rows_run_as_verify_chain(forced, dtype):
     out = {k: v.cpu().numpy() for k, v in out.items()}
     assert not np.isnan(out["p"]).any()
     report(f"unaligned {dtype}", check_chain(b, out))
+
+
+def test_optional_outputs_omitted(forced):
+    b = I.chain_gaussian(20, 6, 5, 4100, "bf16", 2.0, 1.0, 0.8)
+    b.temperature[2] = -1.0
+    d = BD.chain_to_device(b)
+    args = (d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["temperature"])
+    full = BD.sv_verify_chain(*args, lazy=True)
+    bare = BD.sv_verify_chain(*args, lazy=True, want_pq=False, want_status=False)
+    torch.cuda.synchronize()
+    for k in ("tokens", "num_accepted"):
+        assert torch.equal(full[k], bare[k]), k
