@@ -223,3 +223,14 @@ def test_optional_outputs_omitted(forced):
     torch.cuda.synchronize()
     for k in ("tokens", "num_accepted"):
         assert torch.equal(full[k], bare[k]), k
+
+
+def test_large_batch_small_rows(monkeypatch):
+    # 4096 sequences of short rows: large grids on every path (eager, and both early-exit forms).
+    b = I.chain_gaussian(28, 4096, 3, 100, "f32", 2.0, 1.0, 1.0)
+    d = BD.chain_to_device(b)
+    eager = run(b, False, d)
+    check_chain(b, eager, list(range(0, 4096, 37)) + [4095])
+    for form in ("lazy", "staged"):
+        monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", form)
+        assert_same_as_eager(run(b, True, d), eager)
