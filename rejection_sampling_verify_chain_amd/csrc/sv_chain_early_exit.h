@@ -1,0 +1,388 @@
+// Chain verification with early exit (sv_verify_chain_lazy): the one-workgroup form and the
+// staged form.  Source: the Speculative Sampling explainer (0h-n0.github.io, arXiv:2302.01318),
+// Step 3 (ステップ3): the tests run in position order and stop at the first rejection.
+//
+// Included by sv_chain.hip only: the chain, acceptance-rate and sampler kernels form one
+// translation unit, so every kernel template is instantiated and registered once.
+#pragma once
+
+namespace sv {
+namespace {
+
+// ------------------------------------------------------------------------ early exit (positions in order)
+//
+// One workgroup per sequence takes the positions in order: it sweeps target row i and draft row
+// i into LDS, merges them, and tests position i; it stops at the first rejection (residual
+// masses over the same two rows, then the draw) or, after gamma accepts, sweeps target row gamma
+// for the bonus draw.  Rows after the cut are never read.  Each step calls the same device
+// functions as the other paths, so for inputs whose rows are all finite the outputs are theirs
+// bit for bit; only non-finite values in unread rows go unseen.
+
+// Chunks per wave in flight when one workgroup sweeps a row pair: 8 KiB of logits (two bf16
+// chunks measured 2-3% faster here than one, unlike the chip-wide sweeps).
+template <typename T>
+constexpr int kLazyUnits = 4 / int(sizeof(T));
+
+// The draw's records for the row pair in LDS: slot 0 holds target row j <= gamma, slot 1 draft row
+// j > gamma.
+struct PairSrc {
+  const RowStat* st2;  // [2]
+  const RowPart* prt;  // [2][nchunk]
+  const double* wr;    // [nchunk]
+  int64_t nchunk;
+  int gamma;
+  __device__ int slot(int j) const { return j > gamma ? 1 : 0; }
+  __device__ RowStat stat(int j) const { return st2[slot(j)]; }
+  __device__ RowPart part(int j, int64_t c) const { return prt[slot(j) * nchunk + c]; }
+  __device__ RowPart part_lane(int j, int64_t c) const { return prt[slot(j) * nchunk + c]; }
+  __device__ double wres(int64_t c) const { return wr[c]; }
+};
+
+struct LazyShared {
+  RowStat st2[2];
+  int32_t state;  // after a position's test: 0 accepted, 1 rejected, 2 non-finite row
+  int32_t status;
+};
+
+// Chunk partials of rows j0 (slot 0) and, if nrows == 2, j1 (slot 1) into prt (all threads).
+template <typename T, int VW>
+__device__ __forceinline__ void sweep_pair(const ChainParams& p, int64_t b, int j0, int j1,
+                                           int nrows, RowPart* prt, float kk, int wave, int lane) {
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const int nchunk = int(p.nchunk);
+  constexpr int U = kLazyUnits<T>;
+  const int units = nrows * nchunk;
+  for (int w0 = wave * U; w0 < units; w0 += kFusedWaves * U) {
+    RawChunk<T, VW> r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = min(w0 + u, units - 1);
+      const int slot = w / nchunk;
+      const int c = w - slot * nchunk;
+      load_raw<T, VW>(chain_row(tgt, drf, b, p.gamma, slot ? j1 : j0, p.V) + int64_t(c) * kChunk,
+                      chunk_valid(p.V, c), lane, r[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = w0 + u;
+      if (w < units) {  // wave-uniform
+        const int c = w - (w / nchunk) * nchunk;
+        float z[kElemsPerLane];
+        unpack_chunk<T, VW>(r[u], chunk_valid(p.V, c), lane, z);
+        const RowPart rp = reduce_chunk(z, kk);
+        if (lane == 0) prt[w] = rp;
+      }
+    }
+  }
+}
+
+// The fallback result of sequence b (one wave): k = 0, tokens [0, -1, ...], p and q NaN.
+__device__ __forceinline__ void write_fallback(const ChainParams& p, int64_t b, int status,
+                                               int lane) {
+  for (int i = lane; i <= p.gamma; i += kWave) p.out_tokens[b * (p.gamma + 1) + i] = i == 0 ? 0 : -1;
+  for (int i = lane; i < p.gamma; i += kWave) {
+    if (p.out_p) p.out_p[b * p.gamma + i] = NAN;
+    if (p.out_q) p.out_q[b * p.gamma + i] = NAN;
+  }
+  if (lane == 0) {
+    p.out_nacc[b] = 0;
+    if (p.out_status) p.out_status[b] = status;
+  }
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kFusedBlock) void k_chain_lazy(ChainParams p) {
+  extern __shared__ __align__(16) unsigned char lazy_lds[];  // partials [2][nchunk], masses [nchunk]
+  __shared__ LazyShared sh;
+  const int64_t b = blockIdx.x;
+  const int gamma = p.gamma;
+  const int64_t V = p.V, nchunk = p.nchunk;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & (kWave - 1);
+  RowPart* prt = reinterpret_cast<RowPart*>(lazy_lds);
+  double* wr = reinterpret_cast<double*>(lazy_lds + sizeof(RowPart) * 2 * size_t(nchunk));
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const float tb = uniform_load(p.temp, b);
+  const float te = effective_temperature(tb);
+  const double Td = te;
+  const float kk = log2e_over_t(te);
+
+  // Checks that read no logit row: temperature, uniforms, draft tokens.
+  Drafted g{0, false, 0.0f, 0.0f};
+  if (wave == 0) {
+    g = gather_drafted<T>(p, b, lane);
+    int status = 0;
+    if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
+    bool bad = false;
+    for (int i = lane; i <= gamma; i += kWave) {
+      const float u = p.uni[b * (gamma + 1) + i];
+      bad |= !(u >= 0.0f && u < 1.0f);
+    }
+    if (__any(bad)) status |= SV_ROW_BAD_UNIFORM;
+    if (__any(g.bad)) status |= SV_ROW_TOKEN_RANGE;
+    if (lane == 0) sh.status = status;
+  }
+  __syncthreads();
+  if (sh.status != 0) {  // the whole workgroup
+    if (wave == 0) write_fallback(p, b, sh.status, lane);
+    return;
+  }
+
+  int k = gamma;
+  for (int i = 0; i < gamma; ++i) {
+    sweep_pair<T, VW>(p, b, i, gamma + 1 + i, 2, prt, kk, wave, lane);
+    __syncthreads();
+    if (wave < 2) {
+      const RowStat st = merge_row(prt + wave * nchunk, nchunk, lane, Td);
+      if (lane == 0) sh.st2[wave] = st;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const RowStat a = sh.st2[0], d = sh.st2[1];
+      int state = 2;
+      if (a.valid && d.valid) {
+        // Position i's test, on the logits lane i gathered (the eager path's arithmetic).
+        const double zt = __shfl(g.zt, i, kWave), zd = __shfl(g.zd, i, kWave);
+        const double pi = exp((zt - double(a.m)) / Td) / a.s;
+        const double qi = exp((zd - double(d.m)) / Td) / d.s;
+        const double u = p.uni[b * (gamma + 1) + i];
+        const bool accept = qi > 0.0 ? u < fmin(1.0, pi / qi) : (pi > 0.0) && (u < 1.0);
+        if (lane == 0) {
+          if (p.out_p) p.out_p[b * gamma + i] = float(pi);
+          if (p.out_q) p.out_q[b * gamma + i] = float(qi);
+        }
+        state = accept ? 0 : 1;
+      }
+      if (lane == 0) sh.state = state;
+    }
+    __syncthreads();
+    const int state = sh.state;
+    if (state == 2) {
+      if (wave == 0) write_fallback(p, b, SV_ROW_NONFINITE, lane);
+      return;
+    }
+    if (state == 1) {
+      k = i;
+      break;
+    }
+  }
+
+  SeqDecision dec;
+  if (k < gamma) {
+    // Residual masses over the two rows still in LDS.
+    const int jt = k, jd = gamma + 1 + k;
+    for (int64_t c = wave; c < nchunk; c += kFusedWaves) {
+      const int nvalid = chunk_valid(V, c);
+      RawChunk<T, VW> rt, rd;
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jt, V) + c * kChunk, nvalid, lane, rt);
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jd, V) + c * kChunk, nvalid, lane, rd);
+      const double w_c = residual_chunk_mass<T, VW>(rt, rd, nvalid, lane, prt[c],
+                                                    prt[nchunk + c], sh.st2[0], sh.st2[1], Td, kk);
+      if (lane == 0) wr[c] = w_c;
+    }
+    __syncthreads();
+    dec = SeqDecision{k, kDrawResidual, 0, 0};
+  } else {
+    sweep_pair<T, VW>(p, b, gamma, gamma, 1, prt, kk, wave, lane);
+    __syncthreads();
+    if (wave == 0) {
+      const RowStat st = merge_row(prt, nchunk, lane, Td);
+      if (lane == 0) sh.st2[0] = st;
+    }
+    __syncthreads();
+    if (!sh.st2[0].valid) {
+      if (wave == 0) write_fallback(p, b, SV_ROW_NONFINITE, lane);
+      return;
+    }
+    dec = SeqDecision{gamma, kDrawBonus, 0, 0};
+  }
+  if (wave != 0) return;
+  // The accepted prefix, padding, and positions after the cut (never evaluated: p, q NaN).
+  for (int i = lane; i <= gamma; i += kWave)
+    if (i != k) p.out_tokens[b * (gamma + 1) + i] = i < k ? g.x : -1;
+  for (int i = lane; i < gamma; i += kWave) {
+    if (i > k && p.out_p) p.out_p[b * gamma + i] = NAN;
+    if (i > k && p.out_q) p.out_q[b * gamma + i] = NAN;
+  }
+  draw_sequence<T, VW>(p, b, dec, PairSrc{sh.st2, prt, wr, nchunk, gamma});
+}
+
+// ------------------------------------------------------------------------ early exit, staged
+//
+// The positions in order with the whole chip on each: launch j (0 <= j <= gamma + 1) works on
+// every sequence that reached position j - 1, in workgroups that each take a slice of its
+// chunks.  Every workgroup first decides position j - 1 itself (waves 0 and 1 merge the chunk
+// partials of target and draft row j - 1; at j = gamma + 1 only target row gamma, the bonus
+// row), and workgroup 0 writes the sequence's outputs and, at a cut or the bonus row, the
+// decision and row statistics.  After an accept the workgroup sweeps its slice of row pair j
+// (target row gamma alone at j = gamma) into chunk partials and fetches the drafted token's two
+// logits at position j; otherwise it exits.  Launch 0 sweeps pair 0 of every sequence and checks
+// the inputs that need no logit row.  The multi-kernel path's residual and draw kernels then
+// finish every sequence from the decisions.  Rows after the cut are never read, and each step
+// calls the eager path's device functions on the same values, so the outputs agree with
+// sv_verify_chain bit for bit (p and q after the cut excepted).
+
+enum StageRole : int32_t { kStageExit = 0, kStageSweep = 1 };
+
+constexpr int kStageBlock = 256;
+constexpr int kStageWavesPerSimd = 8;
+template <typename T>
+constexpr int kStageUnits = (kStageBlock / kWave) * kUnitsPerWave<T>;  // chunks per workgroup
+
+// Workgroups per sequence in launch j: enough for the largest slice work of that launch.
+inline int stage_groups(int j, int gamma, int64_t nchunk, int units_per_group) {
+  if (j > gamma) return 1;
+  const int64_t units = (j < gamma ? 2 : 1) * nchunk;
+  return int((units + units_per_group - 1) / units_per_group);
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kStageBlock, kStageWavesPerSimd) void k_chain_stage(
+    ChainParams p, int j, int G) {
+  __shared__ RowStat st2[2];
+  __shared__ int32_t role;
+  const int64_t b = blockIdx.x / G;
+  const int g = int(blockIdx.x - b * G);
+  const bool lead = g == 0;  // writes the sequence's outputs
+  const int gamma = p.gamma;
+  const int R = 2 * gamma + 1;
+  const int64_t nchunk = p.nchunk;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & (kWave - 1);
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  const float tb = uniform_load(p.temp, b);
+  const float te = effective_temperature(tb);
+  const double Td = te;
+  const float kk = log2e_over_t(te);
+
+  int r = kStageSweep;
+  if (j == 0) {
+    if (lead && wave == 0) {
+      // Checks that read no logit row; launch 1 takes the fallback on them.
+      int status = 0;
+      if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
+      bool bad = false;
+      for (int i = lane; i <= gamma; i += kWave) {
+        const float u = p.uni[b * (gamma + 1) + i];
+        bad |= !(u >= 0.0f && u < 1.0f);
+      }
+      if (__any(bad)) status |= SV_ROW_BAD_UNIFORM;
+      bad = false;
+      for (int i = lane; i < gamma; i += kWave) {
+        const int x = p.toks[b * gamma + i];
+        bad |= (x < 0) || (int64_t(x) >= p.V);
+      }
+      if (__any(bad)) status |= SV_ROW_TOKEN_RANGE;
+      if (lane == 0) {
+        p.hstat[b] = status;
+        p.alive[b * 2] = 1;
+      }
+    }
+  } else {
+    const int i = j - 1;  // the position decided here; i == gamma: the bonus row
+    if (!uniform_load(p.alive, b * 2 + (i & 1))) {
+      if (lead && threadIdx.x == 0) p.alive[b * 2 + (j & 1)] = 0;
+      return;  // the whole workgroup: the flag is uniform
+    }
+    if (wave < (i < gamma ? 2 : 1)) {
+      const RowStat st = merge_row(p.part + (b * R + (wave == 0 ? i : gamma + 1 + i)) * nchunk,
+                                   nchunk, lane, Td);
+      if (lane == 0) st2[wave] = st;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const RowStat a = st2[0];
+      const RowStat d = i < gamma ? st2[1] : a;
+      int status = i == 0 ? uniform_load(p.hstat, b) : 0;
+      if (!a.valid || !d.valid) status |= SV_ROW_NONFINITE;
+      int rr = kStageExit;
+      if (status != 0) {
+        if (lead) {
+          write_fallback(p, b, status, lane);
+          if (lane == 0) p.seq[b] = SeqDecision{0, kDrawNone, status, 0};
+        }
+      } else if (i == gamma) {
+        if (lead && lane == 0) {
+          p.rowstat[b * R + gamma] = a;
+          p.seq[b] = SeqDecision{gamma, kDrawBonus, 0, 0};
+        }
+      } else {
+        // Position i's test on the logits launch i fetched (the eager path's arithmetic).
+        const int x = uniform_load(p.toks, b * gamma + i);
+        const float zt = uniform_load(p.lz, (b * gamma + i) * 2);
+        const float zd = uniform_load(p.lz, (b * gamma + i) * 2 + 1);
+        const double pi = exp((double(zt) - double(a.m)) / Td) / a.s;
+        const double qi = exp((double(zd) - double(d.m)) / Td) / d.s;
+        const double u = uniform_load(p.uni, b * (gamma + 1) + i);
+        const bool accept = qi > 0.0 ? u < fmin(1.0, pi / qi) : (pi > 0.0) && (u < 1.0);
+        if (lead) {
+          if (lane == 0) {
+            if (p.out_p) p.out_p[b * gamma + i] = float(pi);
+            if (p.out_q) p.out_q[b * gamma + i] = float(qi);
+          }
+          if (accept) {
+            if (lane == 0) p.out_tokens[b * (gamma + 1) + i] = x;
+          } else {
+            // The cut: padding, and positions never evaluated (p, q NaN).
+            for (int t = i + 1 + lane; t <= gamma; t += kWave) {
+              p.out_tokens[b * (gamma + 1) + t] = -1;
+              if (t < gamma && p.out_p) p.out_p[b * gamma + t] = NAN;
+              if (t < gamma && p.out_q) p.out_q[b * gamma + t] = NAN;
+            }
+            if (lane == 0) {
+              p.rowstat[b * R + i] = a;
+              p.rowstat[b * R + gamma + 1 + i] = d;
+              p.seq[b] = SeqDecision{i, kDrawResidual, 0, 0};
+            }
+          }
+        }
+        rr = accept ? kStageSweep : kStageExit;
+      }
+      if (lead && lane == 0) p.alive[b * 2 + (j & 1)] = rr == kStageSweep ? 1 : 0;
+      if (lane == 0) role = rr;
+    }
+    __syncthreads();
+    r = role;
+  }
+
+  constexpr int U = kUnitsPerWave<T>;
+  const int64_t u0 = int64_t(g) * kStageUnits<T> + int64_t(wave) * U;
+  if (r == kStageSweep) {
+    if (lead && wave == 0 && j < gamma) {
+      // The drafted token's logits at position j, for launch j + 1's test.
+      const int x = uniform_load(p.toks, b * gamma + j);
+      if (lane == 0 && x >= 0 && int64_t(x) < p.V) {
+        p.lz[(b * gamma + j) * 2] = widen(chain_row(tgt, drf, b, gamma, j, p.V)[x]);
+        p.lz[(b * gamma + j) * 2 + 1] = widen(chain_row(tgt, drf, b, gamma, gamma + 1 + j, p.V)[x]);
+      }
+    }
+    const int64_t units = (j < gamma ? 2 : 1) * nchunk;
+    RawChunk<T, VW> raw[U];
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int64_t w = min(u0 + t, units - 1);
+      const int row = w < nchunk ? j : gamma + 1 + j;
+      const int64_t c = w < nchunk ? w : w - nchunk;
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, row, p.V) + c * kChunk, chunk_valid(p.V, c),
+                      lane, raw[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int64_t w = u0 + t;
+      if (w < units) {  // wave-uniform
+        const int row = w < nchunk ? j : gamma + 1 + j;
+        const int64_t c = w < nchunk ? w : w - nchunk;
+        float z[kElemsPerLane];
+        unpack_chunk<T, VW>(raw[t], chunk_valid(p.V, c), lane, z);
+        const RowPart rp = reduce_chunk(z, kk);
+        if (lane == 0) p.part[(b * R + row) * nchunk + c] = rp;
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace sv
