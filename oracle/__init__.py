@@ -3,8 +3,11 @@
 This package is a plain, slow, fp64 NumPy statement of what the verify step
 computes.  It exists to check the HIP library against the pages that define the
 method.  Only the test suite, the smoke check and the benchmark's CPU-baseline
-leg may import it; the product path never does, and the oracle imports nothing
-from the product package (the two share no code).
+leg may import it; the product path never does.  The oracle's arithmetic shares no
+code with the product package: the only import from it is the seeded input generator
+(rejection_sampling_verify_chain_amd.inputs, which holds none of the method's
+arithmetic), and only the calibration script calibrate_zipf_sigma.py uses it, to draw
+the workload it calibrates.
 
 Sources (cited by page title and section throughout):
 
@@ -35,7 +38,7 @@ the special cases, and the worked examples under tests/golden/).
 from .chain import (  # noqa: F401
     ROW_TOKEN_RANGE, ROW_NONFINITE, ROW_RESIDUAL_ZERO, ROW_BAD_TREE,
     ROW_BAD_TEMPERATURE, ROW_BAD_UNIFORM, FALLBACK_BITS, BAND,
-    widen, softmax_fp64, verify_chain_seq, verify_chain_batch,
+    widen, softmax_fp64, inverse_cdf, draw_band, verify_chain_seq, verify_chain_batch,
 )
 from .tree import argmax_first, verify_tree_one, verify_tree_batch  # noqa: F401
 from .greedy import verify_chain_greedy_seq, verify_chain_greedy_batch  # noqa: F401

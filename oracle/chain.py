@@ -114,7 +114,9 @@ def inverse_cdf(w, u):
 
     C is the running sum of the non-negative weights w in token-id order and W
     its total, so a token with zero weight is never chosen.  Also returns the
-    distance of u*W to the nearer edge of bucket y, divided by W.
+    distance of u*W to the nearer edge of bucket y, divided by W.  Bucket y is
+    [C(y-1), C(y)) with C(-1) = 0: the lower distance is u*W - C(y-1), the upper
+    one C(y) - u*W.
     """
     c = np.cumsum(w)
     total = c[-1]
@@ -124,6 +126,27 @@ def inverse_cdf(w, u):
     lower = c[y - 1] if y > 0 else 0.0
     edge = min(tau - lower, c[y] - tau) / total
     return y, float(edge)
+
+
+def draw_band(w, u):
+    """Tokens an inverse-CDF draw may return when its running sums and u * W carry an error
+    below BAND * W (the parity band of the draw).
+
+    Token x of positive weight is drawn exactly when u * W falls in its bucket
+    [C(x-1), C(x)); an error of less than BAND * W can move u * W only into a bucket that
+    intersects [u*W - BAND*W, u*W + BAND*W].  So the set holds the exact draw y, the token
+    across each edge of bucket y that lies within the band (the nearest positive-weight
+    neighbour on that side), and further tokens only when a neighbour's whole bucket is
+    narrower than the band.  Zero-weight tokens have empty buckets and never appear.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    c = np.cumsum(w)
+    total = c[-1]
+    tau = u * total
+    b = BAND * total
+    lo = np.concatenate(([0.0], c[:-1]))
+    near = (w > 0.0) & (lo <= tau + b) & (c > tau - b)
+    return {int(x) for x in np.flatnonzero(near)}
 
 
 def _fallback(gamma, status):

@@ -5,8 +5,13 @@ rounding may flip the decision:
 
 * an accept test with |u - min(1, p/q)| < 1e-6: the GPU result must equal the oracle
   replayed with either decision at each such position;
-* a draw with u*W within 1e-6*W of a bucket edge: the GPU token must be the oracle's or the
-  nearest token with positive weight across that edge.
+* a draw with u*W within 1e-6*W of a bucket edge: the GPU token must be one whose bucket
+  lies within 1e-6*W of u*W (oracle.chain.draw_band): the oracle's token, or the nearest
+  positive-weight token across an edge that lies within the band (beyond it only when that
+  neighbour's whole bucket is narrower than the band).
+
+Rows inside a band are counted by kind ("accept_band", "edge_band"); "band_differs" counts
+those where the GPU returned an outcome other than the oracle's own.
 
 Probabilities p_i(x_i), q_i(x_i) must satisfy |gpu - ref| <= 1e-5 * ref + 1e-30.
 """
@@ -32,21 +37,6 @@ ALPHA_RTOL = 1e-5
 ALPHA_ATOL = 1e-12
 
 
-def _neighbours(res):
-    """Tokens the draw may legitimately return for an edge-flagged oracle result."""
-    y = res["tokens"][-1]
-    w = res["weights"]
-    out = {y}
-    pos = np.flatnonzero(w > 0)
-    lower = pos[pos < y]
-    upper = pos[pos > y]
-    if len(lower):
-        out.add(int(lower[-1]))
-    if len(upper):
-        out.add(int(upper[0]))
-    return out
-
-
 def allowed_outcomes(target, draft, toks, uni, temp, res):
     """(k, tokens) pairs the GPU may return for this sequence, with a flag kind."""
     kind = "exact"
@@ -59,11 +49,12 @@ def allowed_outcomes(target, draft, toks, uni, temp, res):
             force = dict(zip(flagged, bits))
             cands.append(OC.verify_chain_seq(target, draft, toks, uni, temp, force=force))
     allowed = set()
+    u_draw = float(uni[-1])
     for r in cands:
         if r["edge"] < OC.BAND:
             if kind == "exact":
                 kind = "edge_band"
-            for y in _neighbours(r):
+            for y in OC.draw_band(r["weights"], u_draw):
                 allowed.add((r["k"], tuple(r["tokens"][:-1]) + (y,)))
         else:
             allowed.add((r["k"], tuple(r["tokens"])))
@@ -76,12 +67,13 @@ def check_chain(batch, out, seqs=None, lazy=False):
     out: dict with tokens [B, gamma+1], num_accepted [B], p, q [B, gamma], status [B].
     lazy: outputs of the early-exit entry point, whose p and q after the cut k are either NaN
     (row not read) or the evaluated values; positions i <= k are checked as usual.
-    Returns counts {"exact": n, "accept_band": n, "edge_band": n, "fallback": n}.
+    Returns counts {"exact": n, "accept_band": n, "edge_band": n, "fallback": n,
+    "band_differs": n} (the last: band rows whose GPU outcome is not the oracle's own).
     Raises AssertionError with a description on the first mismatch.
     """
     B, gamma = batch.B, batch.gamma
     seqs = range(B) if seqs is None else seqs
-    counts = {"exact": 0, "accept_band": 0, "edge_band": 0, "fallback": 0}
+    counts = {"exact": 0, "accept_band": 0, "edge_band": 0, "fallback": 0, "band_differs": 0}
     for b in seqs:
         zt = OC.widen(batch.target[b], batch.dtype)
         zd = OC.widen(batch.draft[b], batch.dtype)
@@ -116,6 +108,8 @@ def check_chain(batch, out, seqs=None, lazy=False):
                                 f"oracle k={res['k']} tokens={res['tokens']} "
                                 f"edge={res['edge']:.3g} flags={res['flag_accept']}")
         counts[kind] += 1
+        if got != (res["k"], tuple(res["tokens"])):
+            counts["band_differs"] += 1
     return counts
 
 
@@ -185,11 +179,11 @@ def check_acceptance_rates(batch, out, seqs=None):
 
 def check_sample(batch, out, rows=None):
     """Compare GPU sampler outputs with the oracle: tokens bit-exact unless the oracle reports the
-    draw within the 1e-6 band of a bucket edge (then the oracle's token or the nearest
-    positive-weight token across that edge), p(y) within the probability bound, status exact.
-    Returns {"exact": n, "edge_band": n, "fallback": n}."""
+    draw within the 1e-6 band of a bucket edge (then a token whose bucket lies within the band,
+    oracle.chain.draw_band), p(y) within the probability bound, status
+    exact.  Returns {"exact": n, "edge_band": n, "fallback": n, "band_differs": n}."""
     rows = range(batch.rows) if rows is None else rows
-    counts = {"exact": 0, "edge_band": 0, "fallback": 0}
+    counts = {"exact": 0, "edge_band": 0, "fallback": 0, "band_differs": 0}
     for r in rows:
         res = OS.sample_row(OC.widen(batch.logits[r], batch.dtype), batch.temperature[r],
                             batch.uniforms[r])
@@ -200,9 +194,10 @@ def check_sample(batch, out, rows=None):
             counts["fallback"] += 1
             continue
         if res["edge"] < OC.BAND:
-            allowed = _neighbours({"tokens": [res["token"]], "weights": res["weights"]})
+            allowed = OC.draw_band(res["weights"], float(batch.uniforms[r]))
             assert y in allowed, (r, y, allowed)
             counts["edge_band"] += 1
+            counts["band_differs"] += int(y != res["token"])
         else:
             assert y == res["token"], (r, y, res["token"])
             counts["exact"] += 1
