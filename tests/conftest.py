@@ -25,3 +25,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def gauss_b256():
+    """The largest chain workload (B=256, gamma=7, V=152064, fp32, T in {0.6, 1.0}) and the
+    oracle's result for every one of its sequences, built once for the tests that check the whole
+    batch on each chain path."""
+    from parity import chain_refs
+    from rejection_sampling_verify_chain_amd import inputs as I
+    b = I.chain_b256_v152064()
+    return b, chain_refs(b)

@@ -61,12 +61,22 @@ def allowed_outcomes(target, draft, toks, uni, temp, res):
     return allowed, kind
 
 
-def check_chain(batch, out, seqs=None, lazy=False):
+def chain_refs(batch, seqs=None):
+    """The oracle's result for each listed sequence of a chain batch ({b: result}), for tests
+    that compare several GPU runs of one batch with the oracle."""
+    seqs = range(batch.B) if seqs is None else seqs
+    return {b: OC.verify_chain_seq(OC.widen(batch.target[b], batch.dtype),
+                                   OC.widen(batch.draft[b], batch.dtype), batch.draft_tokens[b],
+                                   batch.uniforms[b], batch.temperature[b]) for b in seqs}
+
+
+def check_chain(batch, out, seqs=None, lazy=False, refs=None):
     """Compare GPU chain outputs (numpy arrays) with the oracle on the listed sequences.
 
     out: dict with tokens [B, gamma+1], num_accepted [B], p, q [B, gamma], status [B].
     lazy: outputs of the early-exit entry point, whose p and q after the cut k are either NaN
     (row not read) or the evaluated values; positions i <= k are checked as usual.
+    refs: the oracle's results from chain_refs (computed here when absent).
     Returns counts {"exact": n, "accept_band": n, "edge_band": n, "fallback": n,
     "band_differs": n} (the last: band rows whose GPU outcome is not the oracle's own).
     Raises AssertionError with a description on the first mismatch.
@@ -78,7 +88,7 @@ def check_chain(batch, out, seqs=None, lazy=False):
         zt = OC.widen(batch.target[b], batch.dtype)
         zd = OC.widen(batch.draft[b], batch.dtype)
         toks, uni, temp = batch.draft_tokens[b], batch.uniforms[b], batch.temperature[b]
-        res = OC.verify_chain_seq(zt, zd, toks, uni, temp)
+        res = refs[b] if refs is not None else OC.verify_chain_seq(zt, zd, toks, uni, temp)
         st = int(out["status"][b])
         assert st == res["status"], f"seq {b}: status {st} != oracle {res['status']}"
         k = int(out["num_accepted"][b])

@@ -53,11 +53,11 @@ def assert_same_as_eager(lazy, eager):
         assert np.all(np.isnan(a[after]) | (a[after] == b[after])), key
 
 
-def check_both(batch, name, seqs=None):
+def check_both(batch, name, seqs=None, refs=None):
     """Early exit against the oracle and against the eager entry point on the same buffers."""
     d = BD.chain_to_device(batch)
     lazy = run(batch, True, d)
-    report(name, check_chain(batch, lazy, seqs, lazy=True))
+    report(name, check_chain(batch, lazy, seqs, lazy=True, refs=refs))
     assert_same_as_eager(lazy, run(batch, False, d))
     return lazy
 
@@ -171,11 +171,14 @@ def test_batch_threshold_takes_early_exit():
     assert after.any() and np.all(np.isnan(out["p"][after])) and np.all(np.isnan(out["q"][after]))
 
 
-def test_gauss_b256_g7_v152064_sampled():
-    # Full workload, the library's own choice (the early-exit kernel at this batch).
-    b = I.chain_b256_v152064()
-    seqs = list(range(0, 256, 8)) + [1, 2, 3, 255]
-    out = check_both(b, b.name + " sampled", seqs)
+@pytest.mark.parametrize("form", ["auto", "staged", "lazy"])
+def test_gauss_b256_g7_v152064_full(gauss_b256, form, monkeypatch):
+    # Full workload, every sequence: the library's own choice at this batch (the staged form),
+    # and each early-exit form forced.
+    if form != "auto":
+        monkeypatch.setenv("SPECVERIFY_CHAIN_PATH", form)
+    b, refs = gauss_b256
+    out = check_both(b, f"{b.name} {form}", refs=refs)
     after = np.arange(7)[None, :] > out["num_accepted"][:, None]
     assert np.all(np.isnan(out["p"][after]))
 
