@@ -48,7 +48,8 @@ typedef enum {
   SV_ERR_SHAPE = 2,     /* a size is out of range (see each entry point)               */
   SV_ERR_DTYPE = 3,     /* dtype is not an sv_dtype                                    */
   SV_ERR_WORKSPACE = 5, /* workspace is NULL or smaller than the *_workspace_bytes size */
-  SV_ERR_LAUNCH = 6     /* the HIP runtime refused a launch (hipGetLastError)          */
+  SV_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch, or a lookup the call needs */
+  SV_ERR_SCRATCH = 7    /* the call needs more than the library's static scratch holds  */
 } sv_status;
 
 /* Per-sequence / per-tree data-error bits written to out_status (0 = clean). */
@@ -121,6 +122,32 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
                           int32_t* out_tokens, int32_t* out_num_accepted, float* out_p,
                           float* out_q, int32_t* out_status, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Chain verification that allocates nothing, for callers that cannot allocate device memory
+ * during the call or provide a workspace: code under HIP graph capture, tight serving loops,
+ * and harnesses that forbid allocation.
+ *
+ * Exactly sv_verify_chain (same arguments apart from the workspace, same kernels, the same
+ * outputs bit for bit), with its workspace taken from a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
+ * ends.  The call allocates nothing and frees nothing.  Its first call on a device, with that
+ * device current, looks up that device's copy of the array (an error there returns
+ * SV_ERR_LAUNCH).  A call whose workspace (sv_verify_chain_workspace_bytes(B, gamma, V, dtype))
+ * exceeds SV_NOALLOC_SCRATCH_BYTES returns SV_ERR_SCRATCH before launching anything; use
+ * sv_verify_chain with a caller workspace for such shapes.  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (two streams, or two host threads) race and
+ * give undefined results; calls in order on one stream are safe.  Nothing in the array needs
+ * clearing between calls.  Other errors as sv_verify_chain.
+ * ---------------------------------------------------------------------------------------- */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+sv_status sv_verify_chain_noalloc(const void* target_logits, const void* draft_logits,
+                                  sv_dtype dtype, const int32_t* draft_tokens,
+                                  const float* uniforms, const float* temperature, int32_t B,
+                                  int32_t gamma, int64_t V, int32_t* out_tokens,
+                                  int32_t* out_num_accepted, float* out_p, float* out_q,
+                                  int32_t* out_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Chain verification with early exit ([SpS] Step 3: the tests run in order and stop at the first

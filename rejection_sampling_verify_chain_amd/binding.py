@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecveri
 
 SV_F32, SV_BF16 = 0, 1
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_LAUNCH = 0, 1, 2, 3, 5, 6
+SV_ERR_SCRATCH = 7
+NOALLOC_SCRATCH_BYTES = 32 << 20  # SV_NOALLOC_SCRATCH_BYTES
 ROW_TOKEN_RANGE, ROW_NONFINITE, ROW_RESIDUAL_ZERO = 1, 2, 4
 ROW_BAD_TREE, ROW_BAD_TEMPERATURE, ROW_BAD_UNIFORM = 8, 16, 32
 ROW_BAD_INDEX = 64
@@ -29,7 +31,7 @@ EXPORTS = (
     "sv_version", "sv_status_string",
     "sv_verify_chain_workspace_bytes", "sv_verify_chain",
     "sv_verify_chain_with_rates_workspace_bytes", "sv_verify_chain_with_rates",
-    "sv_verify_chain_lazy",
+    "sv_verify_chain_lazy", "sv_verify_chain_noalloc",
     "sv_verify_tree_workspace_bytes", "sv_verify_tree",
     "sv_verify_chain_greedy_workspace_bytes", "sv_verify_chain_greedy",
     "sv_chain_acceptance_rates_workspace_bytes", "sv_chain_acceptance_rates",
@@ -71,6 +73,9 @@ def load():
     lib.sv_verify_chain_lazy.restype = ctypes.c_int
     lib.sv_verify_chain_lazy.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i64,
                                          vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sv_verify_chain_noalloc.restype = ctypes.c_int
+    lib.sv_verify_chain_noalloc.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i64,
+                                            vp, vp, vp, vp, vp, vp]
     lib.sv_verify_chain_with_rates_workspace_bytes.restype = sz
     lib.sv_verify_chain_with_rates_workspace_bytes.argtypes = [i32, i32, i64, ctypes.c_int]
     lib.sv_verify_chain_with_rates.restype = ctypes.c_int
@@ -266,6 +271,44 @@ def sv_verify_chain(target, draft, draft_tokens, uniforms, temperature, *, out_t
     if rates:
         out["alpha"] = out_alpha
     return out
+
+
+def sv_verify_chain_noalloc(target, draft, draft_tokens, uniforms, temperature, *, out_tokens,
+                            out_num_accepted, out_p=None, out_q=None, out_status=None,
+                            stream=None):
+    """Chain verification through the entry point that allocates nothing.
+
+    Same inputs as sv_verify_chain; every output is the caller's (out_p, out_q and out_status
+    may be None, passed as NULL), this function creates no tensor, and the library takes its
+    workspace from its static device scratch.  Raises SpecVerifyError with SV_ERR_SCRATCH when
+    the shape's workspace exceeds NOALLOC_SCRATCH_BYTES.  Returns the dict of output tensors.
+    """
+    lib = load()
+    if target.dtype not in _DTYPE:
+        raise ValueError(f"logits must be float32 or bfloat16, got {target.dtype}")
+    dev = target.device
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    _check(target, "target", None, (B, gamma + 1, V), dev)
+    _check(draft, "draft", target.dtype, (B, gamma, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, gamma), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, gamma + 1), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(out_tokens, "out_tokens", torch.int32, (B, gamma + 1), dev)
+    _check(out_num_accepted, "out_num_accepted", torch.int32, (B,), dev)
+    for t, name, dt, shape in ((out_p, "out_p", torch.float32, (B, gamma)),
+                               (out_q, "out_q", torch.float32, (B, gamma)),
+                               (out_status, "out_status", torch.int32, (B,))):
+        if t is not None:
+            _check(t, name, dt, shape, dev)
+    st = lib.sv_verify_chain_noalloc(
+        _ptr(target), _ptr(draft), _DTYPE[target.dtype], _ptr(draft_tokens), _ptr(uniforms),
+        _ptr(temperature), B, gamma, V, _ptr(out_tokens), _ptr(out_num_accepted), _ptr(out_p),
+        _ptr(out_q), _ptr(out_status), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_verify_chain_noalloc")
+    return {"tokens": out_tokens, "num_accepted": out_num_accepted, "p": out_p, "q": out_q,
+            "status": out_status}
 
 
 def sv_verify_tree(logits, parents, node_tokens, *, out_path=None, out_tokens=None,

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["sv_api.cpp", "sv_trace.cpp", "sv_argmax.hip", "sv_chain.hip", "sv_tree.hip",
-           "sv_greedy.hip", "sv_kv.hip", "sv_probe.hip"]
+           "sv_greedy.hip", "sv_kv.hip", "sv_probe.hip", "sv_noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -65,7 +65,9 @@ SV_EXPORT const char* sv_status_string(sv_status status) {
     case SV_ERR_SHAPE: return "SV_ERR_SHAPE: a size is out of range";
     case SV_ERR_DTYPE: return "SV_ERR_DTYPE: unknown logit dtype";
     case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE: workspace missing, misaligned or too small";
-    case SV_ERR_LAUNCH: return "SV_ERR_LAUNCH: kernel launch failed";
+    case SV_ERR_LAUNCH: return "SV_ERR_LAUNCH: kernel launch (or a runtime lookup) failed";
+    case SV_ERR_SCRATCH:
+      return "SV_ERR_SCRATCH: the call needs more than SV_NOALLOC_SCRATCH_BYTES of scratch";
   }
   return "unknown sv_status";
 }
@@ -127,6 +129,27 @@ SV_EXPORT sv_status sv_verify_chain(const void* target_logits, const void* draft
   return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, temperature, B,
                       gamma, V, out_tokens, out_num_accepted, out_p, out_q, out_status, nullptr,
                       false, workspace, workspace_bytes, stream);
+}
+
+SV_EXPORT sv_status sv_verify_chain_noalloc(const void* target_logits, const void* draft_logits,
+                                            sv_dtype dtype, const int32_t* draft_tokens,
+                                            const float* uniforms, const float* temperature,
+                                            int32_t B, int32_t gamma, int64_t V,
+                                            int32_t* out_tokens, int32_t* out_num_accepted,
+                                            float* out_p, float* out_q, int32_t* out_status,
+                                            hipStream_t stream) {
+  if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !temperature ||
+      !out_tokens || !out_num_accepted)
+    return SV_ERR_NULL;
+  if (!valid_dtype(dtype)) return SV_ERR_DTYPE;
+  if (!chain_shape_ok(B, gamma, V)) return SV_ERR_SHAPE;
+  const size_t need = sv::chain_layout(B, gamma, V).total;
+  if (need > SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (sv::static_scratch(&ws) != hipSuccess) return SV_ERR_LAUNCH;
+  return verify_chain(target_logits, draft_logits, dtype, draft_tokens, uniforms, temperature, B,
+                      gamma, V, out_tokens, out_num_accepted, out_p, out_q, out_status, nullptr,
+                      false, ws, need, stream);
 }
 
 SV_EXPORT sv_status sv_verify_chain_lazy(const void* target_logits, const void* draft_logits,

@@ -264,6 +264,10 @@ hipError_t launch_alpha(const AlphaArgs& a, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 hipError_t launch_kv_compact(const KvArgs& a, hipStream_t stream);
 
+// The current device's copy of the static scratch array of the entry point that allocates
+// nothing (its device address, looked up on the first call on each device).
+hipError_t static_scratch(void** ptr);
+
 // Streaming-read ceiling (measurement support): workgroups the probe launches for `bytes`, and
 // the launch (one output word per workgroup).
 int64_t read_probe_groups(int64_t bytes);

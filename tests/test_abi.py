@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     assert BD.version().startswith("specverify") and "gfx950" in BD.version()
     for st in (BD.SV_OK, BD.SV_ERR_NULL, BD.SV_ERR_SHAPE, BD.SV_ERR_DTYPE, BD.SV_ERR_WORKSPACE,
-               BD.SV_ERR_LAUNCH):
+               BD.SV_ERR_LAUNCH, BD.SV_ERR_SCRATCH):
         assert BD.status_string(st).startswith("SV_")
     assert BD.status_string(99) == "unknown sv_status"
 
@@ -104,6 +104,38 @@ def test_chain_null_pointers(field, entry):
 @pytest.mark.parametrize("entry", CHAIN_ENTRIES)
 def test_chain_validation(kw, status, entry):
     assert chain_call(entry, **kw) == status
+
+
+def noalloc_call(**kw):
+    a = dict(target=FAKE, draft=FAKE, dtype=BD.SV_F32, toks=FAKE, uni=FAKE, temp=FAKE, B=1,
+             gamma=4, V=1000, out_tokens=FAKE, out_nacc=FAKE, out_p=None, out_q=None,
+             out_status=None, stream=None)
+    a.update(kw)
+    return BD.load().sv_verify_chain_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("field", ["target", "draft", "toks", "uni", "temp", "out_tokens",
+                                   "out_nacc"])
+def test_noalloc_null_pointers(field):
+    assert noalloc_call(**{field: None}) == BD.SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), BD.SV_ERR_DTYPE),
+    (dict(B=0), BD.SV_ERR_SHAPE), (dict(gamma=65), BD.SV_ERR_SHAPE), (dict(V=0), BD.SV_ERR_SHAPE),
+    # workspaces beyond the static scratch are refused before anything touches the GPU
+    (dict(B=4096, gamma=7, V=152064), BD.SV_ERR_SCRATCH),
+    (dict(B=1 << 24, gamma=1, V=1), BD.SV_ERR_SCRATCH),
+])
+def test_noalloc_validation(kw, status):
+    assert noalloc_call(**kw) == status
+
+
+def test_noalloc_scratch_limit_matches_workspace_sizes():
+    f = BD.load().sv_verify_chain_workspace_bytes
+    # the largest chain workload fits; sixteen times its batch does not
+    assert f(256, 7, 152064, BD.SV_F32) <= BD.NOALLOC_SCRATCH_BYTES
+    assert f(4096, 7, 152064, BD.SV_F32) > BD.NOALLOC_SCRATCH_BYTES
 
 
 def rates_call(**kw):
