@@ -92,7 +92,9 @@ const char* sv_status_string(sv_status status);
  *   uniforms       fp32 [B, gamma+1]; columns 0..gamma-1 drive the accept tests, column gamma
  *                  the draw.  The caller draws them (the library holds no random state).
  *   temperature    fp32 [B].
- *   B in [1, 2^24], gamma in [1, 64], V in [1, 2^31 - 1].
+ *   B in [1, 2^22 - 1], gamma in [1, 64], V in [1, 2^31 - 1], and
+ *   B * (2*gamma + 1) * ceil(V / 2048) <= 2^26 - 16: every launch stays below 2^32 work-items
+ *   (one wavefront per 2048 logits, one 1024-thread workgroup per sequence); else SV_ERR_SHAPE.
  *   out_tokens        int32 [B, gamma+1]  (required)
  *   out_num_accepted  int32 [B]           (required)
  *   out_p, out_q      fp32 [B, gamma]: p_i(x_i), q_i(x_i) for every i < gamma (optional, NULL)
@@ -215,7 +217,8 @@ sv_status sv_verify_chain_with_rates(const void* target_logits, const void* draf
  *   logits       [n_trees, n_nodes, V] of dtype; row u scores the children of node u.
  *   parents      int32 [n_trees, n_nodes]; parents[t,0] = -1 and 0 <= parents[t,i] < i.
  *   node_tokens  int32 [n_trees, n_nodes]; node 0 holds the last committed token (not emitted).
- *   n_trees in [1, 2^24], n_nodes in [1, 4096], V in [1, 2^31 - 1].
+ *   n_trees in [1, 2^22 - 1], n_nodes in [1, 4096], V in [1, 2^31 - 1], and
+ *   n_trees * n_nodes * ceil(V / 2048) <= 2^26 - 16 (launches below 2^32 work-items).
  *   out_path, out_tokens  int32 [n_trees, n_nodes] (required)
  *   out_num_accepted      int32 [n_trees]          (required)
  *   out_node_argmax       int32 [n_trees, n_nodes] g[u] (optional, NULL)
@@ -249,7 +252,8 @@ sv_status sv_verify_tree(const void* logits, sv_dtype dtype, const int32_t* pare
  *   target_logits  [B, gamma+1, V] of dtype; target row i scores draft token i, row gamma is
  *                  the position after the last draft token.
  *   draft_tokens   int32 [B, gamma].
- *   B in [1, 2^24], gamma in [1, 64], V in [1, 2^31 - 1].
+ *   B in [1, 2^22 - 1], gamma in [1, 64], V in [1, 2^31 - 1], and
+ *   B * (gamma + 1) * ceil(V / 2048) <= 2^26 - 16 (launches below 2^32 work-items).
  *   out_tokens        int32 [B, gamma+1]  (required)
  *   out_num_accepted  int32 [B]           (required)
  *   out_argmax        int32 [B, gamma+1]: g_i (optional, NULL)
@@ -282,7 +286,8 @@ sv_status sv_verify_chain_greedy(const void* target_logits, sv_dtype dtype,
  *   target_logits  [B, gamma+1, V] of dtype (the layout of sv_verify_chain; row gamma is not read).
  *   draft_logits   [B, gamma, V]   of dtype.
  *   temperature    fp32 [B].
- *   B in [1, 2^24], gamma in [1, 64], V in [1, 2^31 - 1].
+ *   B in [1, 2^22 - 1], gamma in [1, 64], V in [1, 2^31 - 1], and
+ *   B * 2*gamma * ceil(V / 2048) <= 2^26 - 16 (launches below 2^32 work-items).
  *   out_alpha      fp32 [B, gamma]  (required)
  *   out_status     int32 [B, gamma]: SV_ROW_* bits of each position (optional, NULL)
  *   workspace      at least sv_chain_acceptance_rates_workspace_bytes(B, gamma, V, dtype)
@@ -313,7 +318,8 @@ sv_status sv_chain_acceptance_rates(const void* target_logits, const void* draft
  *   logits       [rows, V] of dtype, contiguous rows.
  *   temperature  fp32 [rows], finite and > 0.
  *   uniforms     fp32 [rows] in [0, 1), drawn by the caller.
- *   rows >= 1, V in [1, 2^31 - 1] (rows * ceil(V / 2048) / 4 below 2^31).
+ *   rows in [1, 2^22 - 1], V in [1, 2^31 - 1], rows * ceil(V / 2048) <= 2^26 - 16 (launches
+ *   below 2^32 work-items).
  *   out_tokens   int32 [rows] (required)
  *   out_prob     fp32 [rows]: p(y) (optional, NULL)
  *   out_status   int32 [rows]: SV_ROW_* bits (optional, NULL)
@@ -344,7 +350,9 @@ sv_status sv_sample(const void* logits, sv_dtype dtype, const float* temperature
  * Arguments (device pointers, caller-owned):
  *   src           bytes [n, src_rows, row_bytes]: each sequence's speculative KV block.
  *   dst           bytes [n, dst_rows, row_bytes]: each sequence's cache; must not overlap src.
- *   row_bytes     bytes per KV row (all layers, keys and values, of one position), >= 1.
+ *   row_bytes     bytes per KV row (all layers, keys and values, of one position), in
+ *                 [1, 2^40]; n * 8 * ceil(row_bytes / 1024) * 256 below 2^32 (the launch's
+ *                 work-items) and n * max(src_rows, dst_rows) * row_bytes below 2^63.
  *   path          int32 [n, path_len] node ids (-1 padded), or NULL for chains.
  *   num_accepted  int32 [n]; dst_start int32 [n]: first destination row of each sequence.
  *   out_status    int32 [n]: SV_ROW_BAD_INDEX or 0 (optional, NULL).

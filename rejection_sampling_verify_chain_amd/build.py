@@ -4,6 +4,10 @@
 
 Every call compiles from source (no staleness check): the library is small and a
 full build takes seconds.  The result is written atomically next to this file.
+
+Each .hip file is compiled in two passes of the HIP clang driver that hipcc wraps: the device
+pass (gfx950 code object, bundled as a fat binary) carries the device-only flags, and the host
+pass embeds that fat binary and registers its kernels.  Warnings are errors in every pass.
 """
 
 from __future__ import annotations
@@ -29,14 +33,38 @@ def hipcc():
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
+def hip_clang():
+    """The HIP clang driver that hipcc wraps."""
+    return os.environ.get("HIP_CLANG", "/opt/rocm/lib/llvm/bin/clang++")
+
+
 def compile_flags():
-    return [
-        "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off", "-Wall",
-        f"--offload-arch={ARCH}",
-        # Packed fp32 instructions stay off (only scalar fp32 ops in device code).
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", INCLUDE, "-I", CSRC,
-    ]
+    """Flags of every compile pass, host and device: warnings are errors."""
+    return ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off", "-Wall",
+            "-Wextra", "-Werror", "-I", INCLUDE, "-I", CSRC]
+
+
+def device_flags():
+    """Flags of the device pass only: packed fp32 instructions stay off (only scalar fp32 ops in
+    device code).  The host pass does not know this target feature, so it never sees it."""
+    return ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def compile_cmds(src, tmp, extra_flags=()):
+    """Commands that turn one source into an object: a .hip file in two passes (the device code
+    and its fat binary, then the host code that embeds it), a .cpp file in one host pass."""
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(tmp, src + ".o")
+    flags = [*compile_flags(), *extra_flags]
+    if src.endswith(".hip"):
+        fatbin = os.path.join(tmp, src + ".hipfb")
+        return obj, [
+            [hip_clang(), "-x", "hip", f"--offload-arch={ARCH}", "--cuda-device-only", *flags,
+             *device_flags(), path, "-o", fatbin],
+            [hip_clang(), "-x", "hip", f"--offload-arch={ARCH}", "--cuda-host-only", *flags,
+             "-Xclang", "-fcuda-include-gpubinary", "-Xclang", fatbin, "-c", path, "-o", obj],
+        ]
+    return obj, [[hip_clang(), "-x", "hip", "--cuda-host-only", *flags, "-c", path, "-o", obj]]
 
 
 def _run(cmd, verbose):
@@ -45,21 +73,27 @@ def _run(cmd, verbose):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if r.stderr.strip():
+        # -Werror turns compiler diagnostics into errors; anything else a pass prints is shown.
+        print(r.stderr, end="", file=sys.stderr, flush=True)
     return r
 
 
 def build(verbose=False, out_path=LIB_PATH, extra_flags=()):
     """Compile every source and link the shared library; returns its path."""
     with tempfile.TemporaryDirectory(prefix="svbuild_") as tmp:
-        objs = []
-        cmds = []
+        objs, seqs = [], []
         for src in SOURCES:
-            obj = os.path.join(tmp, src + ".o")
+            obj, cmds = compile_cmds(src, tmp, extra_flags)
             objs.append(obj)
-            cmds.append([hipcc(), *compile_flags(), *extra_flags, "-c",
-                         os.path.join(CSRC, src), "-o", obj])
-        with ThreadPoolExecutor(len(cmds)) as ex:
-            list(ex.map(lambda c: _run(c, verbose), cmds))
+            seqs.append(cmds)
+
+        def run_seq(cmds):
+            for c in cmds:
+                _run(c, verbose)
+
+        with ThreadPoolExecutor(len(seqs)) as ex:
+            list(ex.map(run_seq, seqs))
         tmp_lib = os.path.join(tmp, LIB_NAME)
         _run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib],
              verbose)

@@ -18,40 +18,35 @@ int vec_width(sv_dtype dtype) { return dtype == SV_F32 ? 4 : 8; }
 
 bool valid_dtype(sv_dtype dtype) { return dtype == SV_F32 || dtype == SV_BF16; }
 
-// Grid sizes are 32-bit: `units` sequences (or trees) of `rows` logit rows each, one wave per
-// (row, chunk) pair and at least four waves per workgroup.
-bool grid_fits(int64_t units, int64_t rows, int64_t V) {
-  return units * sv::groups_per_unit(rows, V) < int64_t(INT32_MAX);
-}
 
 bool chain_shape_ok(int32_t B, int32_t gamma, int64_t V) {
   if (B < 1 || B > sv::kMaxBatch || gamma < 1 || gamma > sv::kMaxGamma) return false;
   if (V < 1 || V > int64_t(INT32_MAX)) return false;
-  return grid_fits(B, 2 * gamma + 1, V);
+  return sv::shape_grids_fit(B, 2 * gamma + 1, V);
 }
 
 bool tree_shape_ok(int32_t n_trees, int32_t n_nodes, int64_t V) {
   if (n_trees < 1 || n_trees > sv::kMaxBatch || n_nodes < 1 || n_nodes > sv::kMaxTreeNodes)
     return false;
   if (V < 1 || V > int64_t(INT32_MAX)) return false;
-  return grid_fits(n_trees, n_nodes, V);
+  return sv::shape_grids_fit(n_trees, n_nodes, V);
 }
 
 bool greedy_shape_ok(int32_t B, int32_t gamma, int64_t V) {
   if (B < 1 || B > sv::kMaxBatch || gamma < 1 || gamma > sv::kMaxGamma) return false;
   if (V < 1 || V > int64_t(INT32_MAX)) return false;
-  return grid_fits(B, gamma + 1, V);
+  return sv::shape_grids_fit(B, gamma + 1, V);
 }
 
 bool alpha_shape_ok(int32_t B, int32_t gamma, int64_t V) {
   if (B < 1 || B > sv::kMaxBatch || gamma < 1 || gamma > sv::kMaxGamma) return false;
   if (V < 1 || V > int64_t(INT32_MAX)) return false;
-  return grid_fits(B, 2 * gamma, V);
+  return sv::shape_grids_fit(B, 2 * gamma, V);
 }
 
 bool sample_shape_ok(int32_t rows, int64_t V) {
-  if (rows < 1 || V < 1 || V > int64_t(INT32_MAX)) return false;
-  return grid_fits(rows, 1, V);
+  if (rows < 1 || rows > sv::kMaxBatch || V < 1 || V > int64_t(INT32_MAX)) return false;
+  return sv::shape_grids_fit(rows, 1, V);
 }
 
 }  // namespace
@@ -328,13 +323,16 @@ SV_EXPORT sv_status sv_compact_accepted(const void* src, void* dst, int64_t row_
   if (!src || !dst || !num_accepted || !dst_start) return SV_ERR_NULL;
   if (n < 1 || src_rows < 1 || dst_rows < 1 || row_bytes < 1) return SV_ERR_SHAPE;
   if (path && path_len < 1) return SV_ERR_SHAPE;
-  const int64_t src_bytes = int64_t(n) * src_rows * row_bytes;
-  const int64_t dst_bytes = int64_t(n) * dst_rows * row_bytes;
-  // Grid: one block per (sequence, 8 path-slot groups, tile of at least 1 KiB); keep it within
-  // 32 bits.
-  const int64_t tiles = (row_bytes + 1023) / 1024;
-  if (row_bytes > (int64_t(1) << 40) || int64_t(n) * 8 * tiles >= int64_t(INT32_MAX))
+  if (row_bytes > (int64_t(1) << 40)) return SV_ERR_SHAPE;
+  // Buffer sizes in bytes; a product past 2^63 describes no buffer.
+  int64_t src_bytes = 0, dst_bytes = 0;
+  if (__builtin_mul_overflow(int64_t(n) * src_rows, row_bytes, &src_bytes) ||
+      __builtin_mul_overflow(int64_t(n) * dst_rows, row_bytes, &dst_bytes))
     return SV_ERR_SHAPE;
+  // Grid: one workgroup per (sequence, path-slot group, tile of row bytes); it must stay below
+  // 2^32 work-items (n * slots < 2^34 and tiles <= 2^30, so the product fits in 64 bits).
+  const int64_t tiles = sv::ceil_div(row_bytes, sv::kKvMinTileBytes);
+  if (!sv::work_items_fit(int64_t(n) * sv::kKvSlots * tiles, sv::kKvBlock)) return SV_ERR_SHAPE;
   const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
   if (s0 < d0 + uintptr_t(dst_bytes) && d0 < s0 + uintptr_t(src_bytes)) return SV_ERR_SHAPE;
 
@@ -358,7 +356,7 @@ SV_EXPORT sv_status sv_compact_accepted(const void* src, void* dst, int64_t row_
 SV_EXPORT size_t sv_read_probe_out_words(int64_t bytes) {
   if (bytes <= 0 || bytes % 16 != 0) return 0;
   const int64_t g = sv::read_probe_groups(bytes);
-  return g < int64_t(INT32_MAX) ? size_t(g) : 0;
+  return sv::work_items_fit(g, sv::kProbeBlock) ? size_t(g) : 0;
 }
 
 SV_EXPORT sv_status sv_read_probe(const void* src, int64_t bytes, uint32_t* out,

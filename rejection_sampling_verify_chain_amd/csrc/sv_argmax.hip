@@ -88,7 +88,7 @@ hipError_t run(const char* name, const void* logits, int64_t rows, int64_t V, Ar
   const int64_t nchunk = n_chunks(V);
   const int64_t total = rows * nchunk;
   constexpr int wpb = kStreamBlock<T> / kWave;
-  return launch_kernel(name, k_argmax_rows<T, VW>, dim3(unsigned((total + wpb - 1) / wpb)),
+  return launch_kernel(name, k_argmax_rows<T, VW>, dim3(unsigned(wave_groups(total, wpb))),
                        dim3(kStreamBlock<T>), s, logits, V, nchunk, part, total);
 }
 

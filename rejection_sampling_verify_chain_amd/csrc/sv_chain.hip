@@ -247,8 +247,8 @@ enum class LazyForm { kNone, kOneGroup, kStaged };
 // The early-exit form sv_verify_chain_lazy takes (kNone: the eager paths).
 inline LazyForm lazy_form(const ChainArgs& a, int64_t nchunk, int units_per_group,
                           size_t elem_bytes) {
-  const bool staged_ok =
-      int64_t(a.B) * stage_groups(0, a.gamma, nchunk, units_per_group) < int64_t(INT32_MAX);
+  const bool staged_ok = work_items_fit(
+      int64_t(a.B) * stage_groups(0, a.gamma, nchunk, units_per_group), kStageBlock);
   const bool group_ok = lazy_lds_bytes(nchunk) <= kFusedMaxLds;
   const char* e = getenv("SPECVERIFY_CHAIN_PATH");
   if (e && strcmp(e, "staged") == 0) return staged_ok ? LazyForm::kStaged : LazyForm::kNone;
@@ -324,7 +324,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
       const int64_t rtotal = int64_t(a.B) * L.nchunk;
       constexpr int rw = kResidualBlock / kWave;
       const hipError_t e = launch_kernel("chain_residual", k_chain_residual<T, VW>,
-                                         dim3(unsigned((rtotal + rw - 1) / rw)),
+                                         dim3(unsigned(wave_groups(rtotal, rw))),
                                          dim3(kResidualBlock), s, p, rtotal);
       if (e != hipSuccess) return e;
       return launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s,
@@ -342,7 +342,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
   constexpr int wpb = kStreamBlock<T> / kWave;
   hipError_t e = launch_kernel("chain_sweep", k_chain_sweep<T, VW>,
-                               dim3(unsigned((waves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
+                               dim3(unsigned(wave_groups(waves, wpb))), dim3(kStreamBlock<T>), s,
                                p, total);
   if (e != hipSuccess) return e;
   if constexpr (VW > 1) {
@@ -359,7 +359,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   const int64_t rtotal = int64_t(a.B) * L.nchunk;
   constexpr int rw = kResidualBlock / kWave;
   e = launch_kernel("chain_residual", k_chain_residual<T, VW>,
-                    dim3(unsigned((rtotal + rw - 1) / rw)), dim3(kResidualBlock), s, p, rtotal);
+                    dim3(unsigned(wave_groups(rtotal, rw))), dim3(kResidualBlock), s, p, rtotal);
   if (e != hipSuccess) return e;
   e = launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s, p);
   if (e != hipSuccess || !with_rates) return e;

@@ -14,6 +14,7 @@ namespace {
 constexpr int kBlock = 1024;  // decide: one wave per row of a sequence
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kResidualBlock = 256;  // residual: one chunk per wave
+static_assert(kBlock <= kMaxBlock && kResidualBlock <= kMaxBlock, "launch limits of the C ABI");
 
 struct ChainParams {
   const void* tgt;

@@ -30,6 +30,7 @@ namespace {
 //            the HBM peak on 131 MB of bf16, this form at 0.68).
 //   reduce   one wave per (b, i) adds the chunk sums in a fixed order (deterministic).
 constexpr int kAlphaBlock = 256;
+static_assert(kAlphaBlock <= kMaxBlock, "launch limits of the C ABI");
 
 __device__ __forceinline__ int64_t alpha_target_row(const ChainParams& p, int64_t b, int i) {
   return b * (p.tgt_rows + p.gamma) + i;
@@ -132,12 +133,12 @@ hipError_t launch_alpha_tail(const ChainParams& p, int64_t B, double* chunk_sum,
   const int64_t owaves = pairs * p.nchunk;
   constexpr int wpb = kStreamBlock<T> / kWave;
   hipError_t e = launch_kernel("alpha_overlap", k_chain_alpha<T, VW>,
-                               dim3(unsigned((owaves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
+                               dim3(unsigned(wave_groups(owaves, wpb))), dim3(kStreamBlock<T>), s,
                                p, chunk_sum, owaves);
   if (e != hipSuccess) return e;
   constexpr int awpb = kAlphaBlock / kWave;
   return launch_kernel("alpha_reduce", k_chain_alpha_reduce,
-                       dim3(unsigned((pairs + awpb - 1) / awpb)), dim3(kAlphaBlock), s, p,
+                       dim3(unsigned(wave_groups(pairs, awpb))), dim3(kAlphaBlock), s, p,
                        chunk_sum, pairs, out_alpha, out_status);
 }
 
@@ -159,11 +160,11 @@ hipError_t run_alpha(const AlphaArgs& a, hipStream_t s) {
   const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
   constexpr int wpb = kStreamBlock<T> / kWave;
   hipError_t e = launch_kernel("alpha_sweep", k_chain_sweep<T, VW>,
-                               dim3(unsigned((waves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
+                               dim3(unsigned(wave_groups(waves, wpb))), dim3(kStreamBlock<T>), s,
                                p, total);
   if (e != hipSuccess) return e;
   constexpr int awpb = kAlphaBlock / kWave;
-  e = launch_kernel("alpha_merge", k_chain_alpha_merge, dim3(unsigned((rows + awpb - 1) / awpb)),
+  e = launch_kernel("alpha_merge", k_chain_alpha_merge, dim3(unsigned(wave_groups(rows, awpb))),
                     dim3(kAlphaBlock), s, p, rows);
   if (e != hipSuccess) return e;
   return launch_alpha_tail<T, VW>(p, a.B, reinterpret_cast<double*>(a.ws + L.off_chunk_sum),

@@ -114,7 +114,7 @@ hipError_t run_sample(const SampleArgs& a, hipStream_t s) {
   const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
   constexpr int wpb = kStreamBlock<T> / kWave;
   hipError_t e = launch_kernel("sample_sweep", k_chain_sweep<T, VW>,
-                               dim3(unsigned((waves + wpb - 1) / wpb)), dim3(kStreamBlock<T>), s,
+                               dim3(unsigned(wave_groups(waves, wpb))), dim3(kStreamBlock<T>), s,
                                p, total);
   if (e != hipSuccess) return e;
   return launch_kernel("sample_draw", k_sample_draw<T, VW>, dim3(unsigned(a.rows)), dim3(kWave),

@@ -158,6 +158,8 @@ constexpr int kUnitsPerWave = 1;
 // Workgroup size of the streaming kernels (measured): 1024 threads for fp32 logits, 256 for bf16.
 template <typename T>
 constexpr int kStreamBlock = sizeof(T) == 4 ? 1024 : 256;
+static_assert(kStreamBlock<uint16_t> <= kMaxBlock && kStreamBlock<float> <= kMaxBlock,
+              "the C ABI's launch limits assume workgroups of at most kMaxBlock threads");
 
 // Occupancy the vector-load streaming kernels are compiled for: 8 waves per SIMD (at most 64
 // VGPRs, reached without spills).  The one-element-load forms (unaligned rows) are left

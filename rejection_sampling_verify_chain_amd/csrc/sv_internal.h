@@ -19,9 +19,8 @@ constexpr int kElemsPerLane = 32;
 constexpr int kChunk = kWave * kElemsPerLane;  // elements per chunk (2048)
 constexpr int kMaxGamma = 64;
 constexpr int kMaxTreeNodes = 4096;
-constexpr int kMaxBatch = 1 << 24;
+constexpr int kMaxBatch = (1 << 22) - 1;  // one 1024-thread workgroup per sequence: < 2^32 work-items
 
-inline int64_t n_chunks(int64_t V) { return (V + kChunk - 1) / kChunk; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Per (row, chunk) softmax partial: chunk max m and sum_x exp((z(x) - m) / T) in fp64.
@@ -57,12 +56,40 @@ struct __attribute__((aligned(16))) ArgPart {
   int32_t pad;
 };
 
-// Grid sizing for the 32-bit launch limit: workgroups of four waves, one (row, chunk) pair
-// per wave.
-constexpr int kChunksPerGroup = 4;
+// Launch limits.  A dispatch holds its grid size in work-items (workgroups x threads) as a
+// 32-bit number, so every launch must stay below 2^32 work-items.  The launches of an entry
+// point are of two kinds: one wave per chunk (2048 elements) of every logit row it reads, in
+// workgroups of at most kMaxChunkWaves waves, and one workgroup of at most kMaxBlock threads per
+// sequence, tree or row.  shape_grids_fit bounds both for a shape; the launchers static_assert
+// their block sizes against these constants.
+constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
+constexpr int kMaxBlock = 1024;
+constexpr int kMaxChunkWaves = kMaxBlock / kWave;
 
-inline int64_t groups_per_unit(int64_t rows_per_unit, int64_t V) {
-  return (rows_per_unit * n_chunks(V) + kChunksPerGroup - 1) / kChunksPerGroup;
+// ceil(a / b) for a >= 0, b > 0, without forming a + b - 1 (no overflow near INT64_MAX).
+inline int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
+inline int64_t n_chunks(int64_t V) { return ceil_div(V, kChunk); }
+
+// `groups` workgroups of `threads` threads fit one launch.
+inline bool work_items_fit(int64_t groups, int64_t threads) {
+  return groups >= 0 && groups <= kMaxWorkItems / threads;
+}
+
+// Every launch for `units` sequences (trees, rows) of `rows_per_unit` logit rows of V elements
+// fits: the one-wave-per-chunk launches over all units * rows_per_unit * ceil(V / 2048) chunks
+// (rounded up to whole workgroups) and one kMaxBlock-thread workgroup per unit.  The caller
+// bounds units <= 2^31, rows_per_unit <= 4096 and V <= 2^31 - 1 first, so the product stays
+// below 2^63.
+inline bool shape_grids_fit(int64_t units, int64_t rows_per_unit, int64_t V) {
+  const int64_t chunks = units * rows_per_unit * n_chunks(V);
+  return work_items_fit(units, kMaxBlock) && work_items_fit(chunks + kMaxChunkWaves - 1, kWave);
+}
+
+// Workgroups of a launch that gives one wave to each of `units` units, `waves_per_group` waves
+// per workgroup.
+inline int64_t wave_groups(int64_t units, int64_t waves_per_group) {
+  return ceil_div(units, waves_per_group);
 }
 
 // Workspace: per (row, chunk) partials, per row statistics, per sequence decisions, per
@@ -194,6 +221,14 @@ struct SampleArgs {
   bool vec;
 };
 
+// KV compaction geometry: kKvBlock-thread workgroups, each copying one tile of a row for one of
+// kKvSlots groups of path slots; a tile is kKvVecPerThread words per thread, words of 16, 4 or 1
+// bytes by alignment, so at least kKvMinTileBytes.
+constexpr int kKvBlock = 256;
+constexpr int kKvSlots = 8;
+constexpr int kKvVecPerThread = 4;
+constexpr int64_t kKvMinTileBytes = int64_t(kKvBlock) * kKvVecPerThread;
+
 struct KvArgs {
   const void* src;
   void* dst;
@@ -268,9 +303,14 @@ hipError_t launch_kv_compact(const KvArgs& a, hipStream_t stream);
 // nothing (its device address, looked up on the first call on each device).
 hipError_t static_scratch(void** ptr);
 
-// Streaming-read ceiling (measurement support): workgroups the probe launches for `bytes`, and
-// the launch (one output word per workgroup).
-int64_t read_probe_groups(int64_t bytes);
+// Streaming-read ceiling (measurement support): its geometry, the workgroups it launches for
+// `bytes`, and the launch (one output word per workgroup).
+constexpr int kProbeBlock = 1024;
+constexpr int kProbeLoads = 8;                                  // 16-byte loads per lane
+constexpr int64_t kProbeWave16 = int64_t(kWave) * kProbeLoads;  // 16-byte words per wave
+inline int64_t read_probe_groups(int64_t bytes) {
+  return ceil_div(bytes, int64_t(kProbeBlock / kWave) * kProbeWave16 * 16);
+}
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, hipStream_t s);
 
 }  // namespace sv

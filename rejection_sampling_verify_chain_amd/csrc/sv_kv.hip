@@ -20,9 +20,6 @@
 namespace sv {
 namespace {
 
-constexpr int kKvBlock = 256;
-constexpr int kKvVecPerThread = 4;  // 64 bytes per thread per tile with 16-byte vectors
-constexpr int kKvSlots = 8;         // path-slot groups per sequence
 
 struct KvParams {
   const char* src;
@@ -89,7 +86,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv_compact(KvParams p) {
 template <typename VT>
 hipError_t run(KvParams p, hipStream_t s) {
   const int64_t per_tile = int64_t(kKvBlock) * kKvVecPerThread * int64_t(sizeof(VT));
-  p.tiles = (p.row_bytes + per_tile - 1) / per_tile;
+  p.tiles = ceil_div(p.row_bytes, per_tile);
   const int64_t blocks = int64_t(p.n) * kKvSlots * p.tiles;
   return launch_kernel("kv_compact", k_kv_compact<VT>, dim3(unsigned(blocks)), dim3(kKvBlock), s,
                        p);

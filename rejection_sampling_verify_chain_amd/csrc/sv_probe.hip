@@ -12,9 +12,6 @@
 namespace sv {
 namespace {
 
-constexpr int kProbeBlock = 1024;
-constexpr int kProbeLoads = 8;                                  // 16-byte loads per lane
-constexpr int64_t kProbeWave16 = int64_t(kWave) * kProbeLoads;  // 16-byte words per wave
 
 // Each workgroup writes the XOR of every word it read (so no load can be dropped).
 __global__ __launch_bounds__(kProbeBlock, 8) void k_read_probe(const u32x4_t* __restrict__ src,
@@ -43,11 +40,6 @@ __global__ __launch_bounds__(kProbeBlock, 8) void k_read_probe(const u32x4_t* __
 }
 
 }  // namespace
-
-int64_t read_probe_groups(int64_t bytes) {
-  const int64_t per_group = int64_t(kProbeBlock / kWave) * kProbeWave16 * 16;
-  return (bytes + per_group - 1) / per_group;
-}
 
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, hipStream_t s) {
   return launch_kernel("read_probe", k_read_probe, dim3(unsigned(read_probe_groups(bytes))),

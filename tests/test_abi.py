@@ -125,7 +125,7 @@ def test_noalloc_null_pointers(field):
     (dict(B=0), BD.SV_ERR_SHAPE), (dict(gamma=65), BD.SV_ERR_SHAPE), (dict(V=0), BD.SV_ERR_SHAPE),
     # workspaces beyond the static scratch are refused before anything touches the GPU
     (dict(B=4096, gamma=7, V=152064), BD.SV_ERR_SCRATCH),
-    (dict(B=1 << 24, gamma=1, V=1), BD.SV_ERR_SCRATCH),
+    (dict(B=1 << 21, gamma=1, V=1), BD.SV_ERR_SCRATCH),
 ])
 def test_noalloc_validation(kw, status):
     assert noalloc_call(**kw) == status
