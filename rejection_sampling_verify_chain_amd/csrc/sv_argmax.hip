@@ -13,29 +13,42 @@
 namespace sv {
 namespace {
 
-// One wave, one loaded chunk whose first nvalid elements exist -> (max over non-NaN entries,
-// lowest chunk offset holding it (INT32_MAX if none), whether the chunk holds a NaN).  The
-// offset is relative to the chunk start.  Chunk offsets grow with (load j, lane, slot t) in
-// that order, so the lowest offset holding the maximum m is found by ballots instead of a
-// per-element search: the first load whose lane maxima include m, the lowest such lane L, then
-// the first slot of load j in lane L equal to m (one compare per load, one per slot of the
-// found load).  Elements past nvalid are -inf and come after every element in range, so in a
-// row's last chunk a hit at or past nvalid means none in range.  A chunk of only NaN has m =
-// NaN and no hit.
-template <int VW, bool TAIL>
-__device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane], int nvalid) {
+// One wave, one loaded chunk -> (max over non-NaN entries, lowest chunk offset holding it
+// (INT32_MAX if none), whether the chunk holds a NaN).  The offset is relative to the chunk
+// start.  In a row's last chunk the loads past the row repeat its last in-range vector
+// (load_raw), so every element past the row is a copy of an element in range at a lower offset:
+// it cannot change the maximum, the lowest offset holding it, or the NaN test, and needs no
+// masking.  The chunk is taken one load at a time straight from its raw 16-byte vectors (bf16
+// pairs widened on the fly), so no widened copy of the chunk is kept: per load a maximum and a
+// NaN test (unordered compares of element pairs).  Chunk offsets grow with (load j, lane,
+// slot t) in that order, so the lowest offset holding the maximum m is found by ballots instead
+// of a per-element search: the first load whose lane maxima include m, the lowest such lane L,
+// then the first slot of load j in lane L equal to m (that load is widened again: one compare
+// per slot).  A chunk of only NaN has m = NaN and no hit.
+template <typename T, int VW>
+__device__ __forceinline__ ArgPart argmax_chunk(const RawChunk<T, VW>& r) {
   constexpr int NLD = kElemsPerLane / VW;
   float mj[NLD];
   bool nan = false;
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
-    float v = z[j * VW];
+    float z[VW];
+    if constexpr (VW == 1) {
+      z[0] = r.v[j];
+    } else {
+      unpack<T, VW>(r.v[j], z);
+    }
+    float v = z[0];
 #pragma unroll
-    for (int t = 1; t < VW; ++t) v = fmaxf(v, z[j * VW + t]);  // NaN never wins
+    for (int t = 1; t < VW; ++t) v = fmaxf(v, z[t]);  // NaN never wins
     mj[j] = v;
-  }
+    if constexpr (VW == 1) {
+      nan |= z[0] != z[0];
+    } else {
 #pragma unroll
-  for (int i = 0; i < kElemsPerLane; ++i) nan |= (z[i] != z[i]);
+      for (int t = 0; t < VW; t += 2) nan |= __builtin_isunordered(z[t], z[t + 1]);
+    }
+  }
   float lm = mj[0];
 #pragma unroll
   for (int j = 1; j < NLD; ++j) lm = fmaxf(lm, mj[j]);
@@ -46,35 +59,44 @@ __device__ __forceinline__ ArgPart argmax_chunk(const float (&z)[kElemsPerLane],
     const uint64_t h = __ballot(mj[j] == m);
     if (off == INT32_MAX && h != 0) {  // wave-uniform; taken for the first such load only
       const int L = __builtin_ctzll(h);
-      int t_first = VW;
+      int t_first = 0;
+      if constexpr (VW > 1) {
+        float z[VW];
+        unpack<T, VW>(r.v[j], z);
+        t_first = VW;
 #pragma unroll
-      for (int t = VW - 1; t >= 0; --t)
-        if ((__ballot(z[j * VW + t] == m) >> L) & 1) t_first = t;
+        for (int t = VW - 1; t >= 0; --t)
+          if ((__ballot(z[t] == m) >> L) & 1) t_first = t;
+      }
       off = chunk_offset<VW>(j, L, t_first);
     }
   }
-  if (TAIL && off >= nvalid) off = INT32_MAX;
   return ArgPart{m, off, __any(nan) ? 1 : 0, 0};
 }
 
+// Chunks per wave and workgroup size of the streaming argmax: one chunk per wave, workgroups as
+// the softmax sweep's.  Measured on the 16 x 64 x 32000 bf16 tree workload and the 64 x 5 x 128256
+// bf16 greedy workload: two bf16 chunks per wave (8 KiB in flight at 55 VGPRs) gained 1-3% on the
+// first and lost 4-5% on the second; 512- and 1024-thread workgroups lost on both.
+template <typename T>
+constexpr int kArgUnits = 1;
+template <typename T>
+constexpr int kArgBlock = kStreamBlock<T>;
+
 template <typename T, int VW>
-__global__ __launch_bounds__(kStreamBlock<T>, kStreamWavesPerSimd<VW>) void k_argmax_rows(
+__global__ __launch_bounds__(kArgBlock<T>, kStreamWavesPerSimd<VW>) void k_argmax_rows(
     const void* logits_v, int64_t V, int64_t nchunk, ArgPart* part, int64_t total) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t gw = int64_t(blockIdx.x) * (kStreamBlock<T> / kWave) + wave_id();
+  const int64_t gw = int64_t(blockIdx.x) * (kArgBlock<T> / kWave) + wave_id();
   const T* logits = static_cast<const T*>(logits_v);
-  stream_wave<RawChunk<T, VW>, 1>(
+  stream_wave<RawChunk<T, VW>, kArgUnits<T>>(
       gw, total, nchunk, 1,
       [&](const Unit& k, RawChunk<T, VW>& r) {
         load_raw<T, VW>(logits + k.b * V + int64_t(k.c) * kChunk, chunk_valid(V, k.c), lane,
                         r);
       },
       [&](const Unit& k, const RawChunk<T, VW>& r) {
-        const int nvalid = chunk_valid(V, k.c);
-        float z[kElemsPerLane];
-        unpack_chunk<T, VW>(r, nvalid, lane, z);
-        ArgPart a = nvalid == kChunk ? argmax_chunk<VW, false>(z, nvalid)
-                                     : argmax_chunk<VW, true>(z, nvalid);
+        ArgPart a = argmax_chunk<T, VW>(r);
         a.idx = a.idx == INT32_MAX ? INT32_MAX : a.idx + k.c * kChunk;
         if (lane == 0) part[k.w] = a;
       });
@@ -83,13 +105,13 @@ __global__ __launch_bounds__(kStreamBlock<T>, kStreamWavesPerSimd<VW>) void k_ar
 template <typename T, int VW>
 hipError_t run(const char* name, const void* logits, int64_t rows, int64_t V, ArgPart* part,
                hipStream_t s) {
-  // One chunk per wave: at 64 registers the argmax runs 8 waves per SIMD, which measured
-  // faster than two bf16 chunks per wave at the lower occupancy their registers allow.
   const int64_t nchunk = n_chunks(V);
   const int64_t total = rows * nchunk;
-  constexpr int wpb = kStreamBlock<T> / kWave;
-  return launch_kernel(name, k_argmax_rows<T, VW>, dim3(unsigned(wave_groups(total, wpb))),
-                       dim3(kStreamBlock<T>), s, logits, V, nchunk, part, total);
+  constexpr int U = kArgUnits<T>;
+  constexpr int wpb = kArgBlock<T> / kWave;
+  return launch_kernel(name, k_argmax_rows<T, VW>,
+                       dim3(unsigned(wave_groups(wave_groups(total, U), wpb))),
+                       dim3(kArgBlock<T>), s, logits, V, nchunk, part, total);
 }
 
 }  // namespace

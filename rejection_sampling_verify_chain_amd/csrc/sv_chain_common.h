@@ -146,7 +146,7 @@ __device__ int64_t chunk_scan(int64_t c, int64_t V, int lane, double tau_loc, Te
       }
     }
     const uint64_t hit = __ballot(cand >= 0);
-    if (hit) return c * kChunk + __shfl(cand, __builtin_ctzll(hit), kWave);
+    if (hit) return c * kChunk + lane_read(cand, int(__builtin_ctzll(hit)));
     last_pos = max(last_pos, wave_max_int(lp));
     carry += wave_broadcast(incl, kWave - 1);
   }
@@ -368,12 +368,12 @@ __device__ __forceinline__ double locate_batch(const double (&v)[kLocateBatch], 
   if (hit) {
     const int L = __builtin_ctzll(hit);
     ls_state.hit = true;
-    ls_state.at = Located{__shfl(cand, L, kWave), wave_broadcast(cand_before, L), total};
+    ls_state.at = Located{lane_read(cand, L), wave_broadcast(cand_before, L), total};
   }
   const uint64_t pos = __ballot(lp >= 0);
   if (pos) {
     const int L = 63 - __builtin_clzll(pos);
-    ls_state.last_c = __shfl(lp, L, kWave);
+    ls_state.last_c = lane_read(lp, L);
     ls_state.last_before = wave_broadcast(lp_before, L);
   }
   return wave_broadcast(incl, kWave - 1);

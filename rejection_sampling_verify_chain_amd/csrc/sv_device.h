@@ -257,6 +257,12 @@ __device__ __forceinline__ int lane_read(int v, int l) { return __builtin_amdgcn
 __device__ __forceinline__ float lane_read(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
+__device__ __forceinline__ int64_t lane_read(int64_t v, int l) {
+  const uint64_t u = uint64_t(v);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), l));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
 __device__ __forceinline__ double lane_read(double v, int l) {
   const uint64_t u = __double_as_longlong(v);
   const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), l));
@@ -289,17 +295,35 @@ __device__ __forceinline__ int wave_max_int(int v) {
   return wave_allreduce(v, [](int a, int b) { return max(a, b); });
 }
 
-// Inclusive prefix sum over the lanes of a wave (Hillis-Steele).
-__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
+// Row shift right by N lanes inside each row of 16 lanes (dpp_ctrl row_shr:N); a lane whose
+// source would lie before its row's first lane reads 0.
+template <int N>
+__device__ __forceinline__ double dpp_shr_zero(double v) {
+  static_assert(N >= 1 && N <= 15, "row_shr takes 1..15");
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(u)), 0x110 + N, 0xF, 0xF, true));
+  const uint32_t hi =
+      uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(u >> 32)), 0x110 + N, 0xF, 0xF, true));
+  return __longlong_as_double((uint64_t(hi) << 32) | lo);
 }
 
-__device__ __forceinline__ double wave_broadcast(double v, int src) { return __shfl(v, src, kWave); }
+// Inclusive prefix sum over the lanes of a wave, fp64, in the vector ALU: four DPP shift-and-add
+// steps (1, 2, 4, 8 lanes) give each lane the prefix inside its row of 16; the totals of rows 0-2
+// (lanes 15, 31, 47) are then read out and added to the later rows in one fixed order.  Every
+// caller sums its lanes this way, so a sum recomputed by another kernel has the same bits.
+__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
+  v += dpp_shr_zero<1>(v);
+  v += dpp_shr_zero<2>(v);
+  v += dpp_shr_zero<4>(v);
+  v += dpp_shr_zero<8>(v);
+  const double r0 = lane_read(v, 15), r1 = lane_read(v, 31), r2 = lane_read(v, 47);
+  const int row = lane >> 4;
+  const double off = row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+  return row == 0 ? v : v + off;
+}
+
+// The value of lane `src` (wave-uniform) in every lane.
+__device__ __forceinline__ double wave_broadcast(double v, int src) { return lane_read(v, src); }
 
 // Index of the calling wave within its workgroup, as a wave-uniform (scalar) value: index
 // arithmetic derived from it runs on the scalar unit instead of every lane.

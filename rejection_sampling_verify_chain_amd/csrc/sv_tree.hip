@@ -10,12 +10,13 @@
 //   argmax  the single HBM sweep (launch_argmax_rows): each wave owns one chunk (2048
 //           elements) of one node's logit row and writes the chunk maximum over non-NaN entries
 //           and the lowest index attaining it.
-//   walk    one workgroup per tree merges the partials into g[u] for every node, validates
-//           the parent array, and builds a child table in LDS: next[u] = the lowest-id child c
-//           with parent u and token g[u] (an LDS atomic minimum over the nodes).  Following
-//           next[] from the root gives the accepted path; g of its last node is the bonus token.
-//           All global loads of the tree (partials, parents, tokens) are issued together, so
-//           the walk takes one memory round trip before its stores.
+//   walk    merges the partials into g[u] for every node, validates the parent array, and
+//           follows, from the root, the lowest-id child c of the current node u whose token is
+//           g[u]; g of the last node reached is the bonus token.  Trees of up to 64 nodes take
+//           one wave per tree (k_tree_walk_wave: a lane per node, one ballot per step); larger
+//           ones one workgroup per tree with a child table in LDS (next[u], an LDS atomic
+//           minimum over the nodes).  All global loads of the tree (partials, parents, tokens)
+//           are issued together, so the walk takes one memory round trip before its stores.
 
 #include <math.h>
 
@@ -179,6 +180,89 @@ __device__ void finish_tree(const TreeParams& p, int64_t t, const WalkShared& sh
   }
 }
 
+// Trees of at most 64 nodes: one wave per tree, lane u = node u, no LDS and no barrier.  Each
+// lane merges its node's chunk partials (all loads in flight together), reads its parent's argmax
+// with one cross-lane read, and marks itself matched when its token equals it.  The walk is one
+// ballot per step: the lowest matched child of the current node.  Children have larger ids than
+// their parents, so the nodes of the accepted path sorted by id are in path order, and a node's
+// place on the path is the number of path nodes below its id: every output is written in
+// parallel.  The same result as finish_tree: the lowest-id matching child at every step, the
+// argmax order of merge_row_argmax, and the same validation and fallback.
+constexpr int kWalkWaveBatch = 16;  // partials a lane loads at once
+
+__global__ __launch_bounds__(kWave) void k_tree_walk_wave(TreeParams p) {
+  const int64_t t = blockIdx.x;
+  const int n = p.n_nodes;
+  const int lane = threadIdx.x;
+  const int64_t base = t * n;
+  const bool live = lane < n;
+  const int32_t par = live ? p.parents[base + lane] : 0;
+  const int32_t tok = live ? p.node_tokens[base + lane] : 0;
+
+  float best = -INFINITY;
+  int32_t bidx = INT32_MAX;
+  int anynan = 0;
+  if (live) {
+    const ArgPart* pp = p.part + (base + lane) * p.nchunk;
+    for (int64_t c0 = 0; c0 < p.nchunk; c0 += kWalkWaveBatch) {
+      ArgPart r[kWalkWaveBatch];
+#pragma unroll
+      for (int i = 0; i < kWalkWaveBatch; ++i)
+        r[i] = c0 + i < p.nchunk ? pp[c0 + i] : ArgPart{-INFINITY, INT32_MAX, 0, 0};
+#pragma unroll
+      for (int i = 0; i < kWalkWaveBatch; ++i) {
+        if (arg_better(r[i].v, r[i].idx, best, bidx)) {
+          best = r[i].v;
+          bidx = r[i].idx;
+        }
+        anynan |= r[i].nan;
+      }
+    }
+  }
+  const int32_t g = bidx == INT32_MAX ? 0 : bidx;
+  if (p.out_g && live) p.out_g[base + lane] = g;
+
+  const bool bad_tree = live && (lane == 0 ? par != -1 : (par < 0 || par >= lane));
+  const bool bad_tok = live && lane > 0 && (tok < 0 || int64_t(tok) >= p.V);
+  const int status = (__any(bad_tree) ? SV_ROW_BAD_TREE : 0) |
+                     (__any(bad_tok) ? SV_ROW_TOKEN_RANGE : 0) |
+                     (__any(anynan) ? SV_ROW_NONFINITE : 0);
+  // g of this node's parent (lanes whose parent index is out of range read lane 0; they are
+  // either the root or a bad tree, which is not walked).
+  const int32_t gp = __shfl(g, (par >= 0 && par < kWave) ? par : 0, kWave);
+  const bool match = live && lane > 0 && par >= 0 && par < lane && tok == gp;
+
+  uint64_t path = 0;  // accepted nodes other than the root
+  int u = 0, k = 0;
+  if (!(status & (SV_ROW_BAD_TREE | SV_ROW_TOKEN_RANGE))) {
+    for (;;) {  // at most n - 1 steps: every step moves to a larger node id
+      const uint64_t kids = __ballot(match && par == u);
+      if (kids == 0) break;
+      u = __builtin_ctzll(kids);
+      path |= uint64_t(1) << u;
+      ++k;
+    }
+  }
+  const int32_t bonus = __shfl(g, u, kWave);
+  if (live) {
+    if ((path >> lane) & 1) {
+      const int pos = __popcll(path & ((uint64_t(1) << lane) - 1));  // 0-based place on the path
+      p.out_path[base + pos + 1] = lane;
+      p.out_tokens[base + pos] = tok;
+    }
+    if (lane == 0) p.out_path[base] = 0;
+    if (lane > k) {
+      p.out_path[base + lane] = -1;
+      p.out_tokens[base + lane] = -1;
+    }
+    if (lane == k) p.out_tokens[base + k] = bonus;
+  }
+  if (lane == 0) {
+    p.out_nacc[t] = k;
+    if (p.out_status) p.out_status[t] = status;
+  }
+}
+
 __global__ __launch_bounds__(kWalkBlock) void k_tree_walk(TreeParams p) {
   extern __shared__ int32_t walk_lds[];
   __shared__ int32_t flags;
@@ -205,6 +289,9 @@ hipError_t run_tree(const TreeArgs& a, hipStream_t s) {
   const hipError_t e = launch_argmax_rows("tree_argmax", a.logits, a.dtype, a.vec,
                                           int64_t(a.n_trees) * a.n_nodes, a.V, p.part, s);
   if (e != hipSuccess) return e;
+  if (a.n_nodes <= kWave)
+    return launch_kernel("tree_walk", k_tree_walk_wave, dim3(unsigned(a.n_trees)), dim3(kWave), s,
+                         p);
   return launch_kernel_shm("tree_walk", k_tree_walk, dim3(unsigned(a.n_trees)), dim3(kWalkBlock),
                            size_t(3) * sizeof(int32_t) * size_t(a.n_nodes), s, p);
 }
