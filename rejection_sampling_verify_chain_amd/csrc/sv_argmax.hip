@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "sv_argmax.h"
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -74,22 +76,17 @@ __device__ __forceinline__ ArgPart argmax_chunk(const RawChunk<T, VW>& r) {
   return ArgPart{m, off, __any(nan) ? 1 : 0, 0};
 }
 
-// Chunks per wave and workgroup size of the streaming argmax: one chunk per wave, workgroups as
-// the softmax sweep's.  Measured on the 16 x 64 x 32000 bf16 tree workload and the 64 x 5 x 128256
-// bf16 greedy workload: two bf16 chunks per wave (8 KiB in flight at 55 VGPRs) gained 1-3% on the
-// first and lost 4-5% on the second; 512- and 1024-thread workgroups lost on both.
-template <typename T>
-constexpr int kArgUnits = 1;
+// Workgroup size of the streaming argmax: as the softmax sweep's.
 template <typename T>
 constexpr int kArgBlock = kStreamBlock<T>;
 
-template <typename T, int VW>
+template <typename T, int VW, int U>
 __global__ __launch_bounds__(kArgBlock<T>, kStreamWavesPerSimd<VW>) void k_argmax_rows(
     const void* logits_v, int64_t V, int64_t nchunk, ArgPart* part, int64_t total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t gw = int64_t(blockIdx.x) * (kArgBlock<T> / kWave) + wave_id();
   const T* logits = static_cast<const T*>(logits_v);
-  stream_wave<RawChunk<T, VW>, kArgUnits<T>>(
+  stream_wave<RawChunk<T, VW>, U>(
       gw, total, nchunk, 1,
       [&](const Unit& k, RawChunk<T, VW>& r) {
         load_raw<T, VW>(logits + k.b * V + int64_t(k.c) * kChunk, chunk_valid(V, k.c), lane,
@@ -102,15 +99,41 @@ __global__ __launch_bounds__(kArgBlock<T>, kStreamWavesPerSimd<VW>) void k_argma
       });
 }
 
+// Chunks per wave.  A bf16 launch whose chunks fit one round of resident waves at two chunks per
+// wave (but not at one) takes two: every chunk's loads are then issued at the start, with no second
+// round of waves waiting for the first to finish.  Otherwise one chunk per wave: finer waves
+// shorten the last round's tail.  Measured on bf16 rows: the 16 x 64 x 32000 tree workload
+// (16384 chunks, one round at two per wave) 12.6 -> 12.2 us; the 64 x 5 x 128256 greedy workload
+// (20160 chunks, 1.23 rounds at two per wave) 14.2 us at one chunk per wave against 15.1 at two.
+// 512- and 1024-thread workgroups were slower for both.
+int resident_waves(int waves_per_simd) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n * 4 * waves_per_simd;  // four SIMDs per compute unit
+}
+
 template <typename T, int VW>
 hipError_t run(const char* name, const void* logits, int64_t rows, int64_t V, ArgPart* part,
                hipStream_t s) {
   const int64_t nchunk = n_chunks(V);
   const int64_t total = rows * nchunk;
-  constexpr int U = kArgUnits<T>;
   constexpr int wpb = kArgBlock<T> / kWave;
-  return launch_kernel(name, k_argmax_rows<T, VW>,
-                       dim3(unsigned(wave_groups(wave_groups(total, U), wpb))),
+  const int64_t slots = resident_waves(kStreamWavesPerSimd<VW>);
+  if constexpr (sizeof(T) == 2 && VW > 1) {  // 4 KiB chunks; an fp32 chunk is already 8 KiB
+    if (total > slots && total <= 2 * slots)
+      return launch_kernel(name, k_argmax_rows<T, VW, 2>,
+                           dim3(unsigned(wave_groups(wave_groups(total, 2), wpb))),
+                           dim3(kArgBlock<T>), s, logits, V, nchunk, part, total);
+  }
+  return launch_kernel(name, k_argmax_rows<T, VW, 1>, dim3(unsigned(wave_groups(total, wpb))),
                        dim3(kArgBlock<T>), s, logits, V, nchunk, part, total);
 }
 

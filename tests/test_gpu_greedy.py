@@ -101,3 +101,29 @@ def test_deterministic():
         again = run_greedy(b)
         for k in first:
             assert np.array_equal(first[k], again[k])
+
+
+def test_two_chunks_per_wave_odd_chunk_count():
+    # 61 sequences x 5 target rows x 33 chunks (V = 66000) = 10065 chunks: more than one round of
+    # resident waves at one chunk per wave and at most one at two, so the argmax takes two chunks
+    # per wave, and the last wave holds a single chunk.  Ties, signed zeros and NaN sit in the
+    # second chunk of a wave's pair and across the pair's boundary.
+    B, gamma, V = 61, 4, 66000
+    rng = np.random.default_rng(77)
+    z = rng.normal(scale=2.0, size=(B, gamma + 1, V)).astype(np.float32)
+    rows = z.reshape(-1, V)
+    for r in range(0, rows.shape[0], 7):
+        rows[r, [4096 + 17, 6144 + 3, 2047]] = 30.0            # ties across chunks 1..3
+    for r in range(3, rows.shape[0], 11):
+        rows[r, :] = -1.0
+        rows[r, 2048 + 5], rows[r, 2048 + 1] = -0.0, 0.0        # both zeros in the second chunk
+    rows[5, 2049] = np.nan                                     # NaN flagged, never the maximum
+    rows[rows.shape[0] - 1, V - 1] = 40.0                      # maximum in the lone last chunk
+    plant = np.argmax(z, axis=2)
+    toks = np.where(rng.random((B, gamma)) < 0.7, plant[:, :gamma],
+                    rng.integers(0, V, size=(B, gamma))).astype(np.int32)
+    b = I.GreedyBatch("two_chunks", "f32", z, toks)
+    out = run_greedy(b)
+    check_chain_greedy(b, out)
+    bb = I.GreedyBatch("two_chunks_bf16", "bf16", I.bf16_bits(z), toks)
+    check_chain_greedy(bb, run_greedy(bb))
