@@ -15,25 +15,14 @@
 namespace sv {
 namespace {
 
-// One wave, one loaded chunk -> (max over non-NaN entries, lowest chunk offset holding it
-// (INT32_MAX if none), whether the chunk holds a NaN).  The offset is relative to the chunk
-// start.  In a row's last chunk the loads past the row repeat its last in-range vector
-// (load_raw), so every element past the row is a copy of an element in range at a lower offset:
-// it cannot change the maximum, the lowest offset holding it, or the NaN test, and needs no
-// masking.  The chunk is taken one load at a time straight from its raw 16-byte vectors (bf16
-// pairs widened on the fly), so no widened copy of the chunk is kept: per load a maximum and a
-// NaN test (unordered compares of element pairs).  Chunk offsets grow with (load j, lane,
-// slot t) in that order, so the lowest offset holding the maximum m is found by ballots instead
-// of a per-element search: the first load whose lane maxima include m, the lowest such lane L,
-// then the first slot of load j in lane L equal to m (that load is widened again: one compare
-// per slot).  A chunk of only NaN has m = NaN and no hit.
-template <typename T, int VW>
-__device__ __forceinline__ ArgPart argmax_chunk(const RawChunk<T, VW>& r) {
-  constexpr int NLD = kElemsPerLane / VW;
-  float mj[NLD];
-  bool nan = false;
+// Per-load maxima of a lane's elements (load j holds VW of them, widened from its raw 16-byte
+// vector).  NANPROP: NaN-propagating maxima (v_maximum3_f32, no canonicalisation of the inputs), so
+// a maximum is NaN exactly when its elements hold a NaN; otherwise NaN-ignoring ones (fmaxf).
+template <bool NANPROP, typename T, int VW>
+__device__ __forceinline__ void load_maxima(const RawChunk<T, VW>& r,
+                                            float (&mj)[kElemsPerLane / VW]) {
 #pragma unroll
-  for (int j = 0; j < NLD; ++j) {
+  for (int j = 0; j < kElemsPerLane / VW; ++j) {
     float z[VW];
     if constexpr (VW == 1) {
       z[0] = r.v[j];
@@ -42,19 +31,44 @@ __device__ __forceinline__ ArgPart argmax_chunk(const RawChunk<T, VW>& r) {
     }
     float v = z[0];
 #pragma unroll
-    for (int t = 1; t < VW; ++t) v = fmaxf(v, z[t]);  // NaN never wins
+    for (int t = 1; t < VW; ++t) v = NANPROP ? __builtin_elementwise_maximum(v, z[t]) : fmaxf(v, z[t]);
     mj[j] = v;
-    if constexpr (VW == 1) {
-      nan |= z[0] != z[0];
-    } else {
-#pragma unroll
-      for (int t = 0; t < VW; t += 2) nan |= __builtin_isunordered(z[t], z[t + 1]);
-    }
   }
+}
+
+// One wave, one loaded chunk -> (max over non-NaN entries, lowest chunk offset holding it
+// (INT32_MAX if none), whether the chunk holds a NaN).  The offset is relative to the chunk
+// start.  In a row's last chunk the loads past the row repeat its last in-range vector
+// (load_raw), so every element past the row is a copy of an element in range at a lower offset:
+// it cannot change the maximum, the lowest offset holding it, or the NaN test, and needs no
+// masking.  The chunk is taken one load at a time straight from its raw 16-byte vectors (bf16
+// pairs widened on the fly), so no widened copy of the chunk is kept.  The per-load maxima are
+// first taken NaN-propagating, which also tests for NaN (a lane whose maximum is NaN); only a
+// chunk that holds a NaN takes them again NaN-ignoring.  Chunk offsets grow with (load j, lane,
+// slot t) in that order, so the lowest offset holding the maximum m is found by ballots instead
+// of a per-element search: the first load whose lane maxima include m, the lowest such lane L,
+// then the first slot of load j in lane L equal to m (that load is widened again: one compare
+// per slot).  -0 equals +0 in these compares, so either sign of a zero maximum finds the lowest
+// zero.  A chunk of only NaN has m = NaN and no hit.
+template <typename T, int VW>
+__device__ __forceinline__ ArgPart argmax_chunk(const RawChunk<T, VW>& r) {
+  constexpr int NLD = kElemsPerLane / VW;
+  float mj[NLD];
+  load_maxima<true>(r, mj);
   float lm = mj[0];
 #pragma unroll
-  for (int j = 1; j < NLD; ++j) lm = fmaxf(lm, mj[j]);
-  const float m = wave_max(lm);
+  for (int j = 1; j < NLD; ++j) lm = __builtin_elementwise_maximum(lm, mj[j]);
+  const bool nan = __any(lm != lm);  // wave-uniform
+  float m;
+  if (!nan) {
+    m = wave_allreduce(lm, [](float a, float b) { return __builtin_elementwise_maximum(a, b); });
+  } else {
+    load_maxima<false>(r, mj);
+    lm = mj[0];
+#pragma unroll
+    for (int j = 1; j < NLD; ++j) lm = fmaxf(lm, mj[j]);
+    m = wave_max(lm);
+  }
   int off = INT32_MAX;
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
@@ -73,7 +87,7 @@ __device__ __forceinline__ ArgPart argmax_chunk(const RawChunk<T, VW>& r) {
       off = chunk_offset<VW>(j, L, t_first);
     }
   }
-  return ArgPart{m, off, __any(nan) ? 1 : 0, 0};
+  return ArgPart{m, off, nan ? 1 : 0, 0};
 }
 
 // Workgroup size of the streaming argmax: as the softmax sweep's.
