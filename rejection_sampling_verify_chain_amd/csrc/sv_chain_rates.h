@@ -23,7 +23,9 @@ namespace {
 //            of target row i and draft row i, where e_t, e_d are the chunk-local softmax terms,
 //            A and B the chunk scales taking them to p and q, s = max(A, B) and
 //            (ra, rb) = (A, B) / s (one of them is 1, the other at most 1, so nothing
-//            overflows).  A chunk where A or B is 0 adds nothing.  The chunk loads go out first;
+//            overflows); for bf16 rows with one exponential per element: min(ra e_t, rb e_d)
+//            is 2 to the smaller of the two exponents, one of them offset by log2 of its
+//            ratio.  A chunk where A or B is 0 adds nothing.  The chunk loads go out first;
 //            the row statistics and chunk partials arrive through the scalar cache meanwhile.
 //            Workgroups are sized like the sweep's (measured: 1024 threads for fp32, 256 for
 //            bf16; a workgroup per (b, i) with waves looping over the chunks ran at 0.47 of
@@ -46,8 +48,14 @@ __global__ __launch_bounds__(kAlphaBlock) void k_chain_alpha_merge(ChainParams p
   if (lane == 0) p.rowstat[r] = st;
 }
 
+// Waves per SIMD of the overlap kernel: five for 16-byte bf16 loads (at most 96 VGPRs); the
+// fp32 kernel's 1024-thread workgroup already implies four, and the one-element-load form is
+// left unbounded.
 template <typename T, int VW>
-__global__ __launch_bounds__(kStreamBlock<T>) void k_chain_alpha(ChainParams p, double* chunk_sum,
+constexpr int kAlphaWavesPerSimd = sizeof(T) == 2 && VW > 1 ? 5 : 1;
+
+template <typename T, int VW>
+__global__ __launch_bounds__(kStreamBlock<T>, (kAlphaWavesPerSimd<T, VW>)) void k_chain_alpha(ChainParams p, double* chunk_sum,
                                                                 int64_t total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t w = int64_t(blockIdx.x) * (kStreamBlock<T> / kWave) + wave_id();
@@ -79,10 +87,32 @@ __global__ __launch_bounds__(kStreamBlock<T>) void k_chain_alpha(ChainParams p, 
       unpack_chunk<T, VW>(rt, nvalid, lane, zt);
       unpack_chunk<T, VW>(rd, nvalid, lane, zd);
       const double sc = fmax(A, Bq);
-      const float ra = float(A / sc), rb = float(Bq / sc);
-      acc = sc * wave_sum(lane_term_sum([&](int e) {
-              return fminf(ra * softmax_term(zt[e], ct.m, kk), rb * softmax_term(zd[e], cd.m, kk));
-            }));
+      if constexpr (sizeof(T) == 2) {
+        // bf16 rows are short and bound by the per-element work: min(ra e_t, rb e_d) is taken
+        // as 2^min(x_t + log2 ra, x_d + log2 rb), x = (z - m_c) log2(e) / T, one exponential
+        // per element instead of two.  One of ra, rb is exactly 1 (log 0), so only the other
+        // side takes an offset.  A ratio below 2^-149 gives -inf (a term of 0, as ra = 0 does
+        // in the product form).
+        double s;
+        if (A < Bq) {  // wave-uniform
+          const float off = log2f(float(A / sc));
+          s = wave_sum(lane_term_sum([&](int e) {
+            return hw_exp2(fminf((zt[e] - ct.m) * kk + off, (zd[e] - cd.m) * kk));
+          }));
+        } else {
+          const float off = log2f(float(Bq / sc));
+          s = wave_sum(lane_term_sum([&](int e) {
+            return hw_exp2(fminf((zt[e] - ct.m) * kk, (zd[e] - cd.m) * kk + off));
+          }));
+        }
+        acc = sc * s;
+      } else {
+        // fp32 rows are bound by HBM; the product form keeps the kernel's registers lower.
+        const float ra = float(A / sc), rb = float(Bq / sc);
+        acc = sc * wave_sum(lane_term_sum([&](int e) {
+                return fminf(ra * softmax_term(zt[e], ct.m, kk), rb * softmax_term(zd[e], cd.m, kk));
+              }));
+      }
     }
   }
   if (lane == 0) chunk_sum[w] = acc;
