@@ -351,7 +351,7 @@ sv_status sv_sample(const void* logits, sv_dtype dtype, const float* temperature
  *   src           bytes [n, src_rows, row_bytes]: each sequence's speculative KV block.
  *   dst           bytes [n, dst_rows, row_bytes]: each sequence's cache; must not overlap src.
  *   row_bytes     bytes per KV row (all layers, keys and values, of one position), in
- *                 [1, 2^40]; n * 8 * ceil(row_bytes / 1024) * 256 below 2^32 (the launch's
+ *                 [1, 2^40]; n * 8 * ceil(row_bytes / 512) * 256 below 2^32 (the launch's
  *                 work-items) and n * max(src_rows, dst_rows) * row_bytes below 2^63.
  *   path          int32 [n, path_len] node ids (-1 padded), or NULL for chains.
  *   num_accepted  int32 [n]; dst_start int32 [n]: first destination row of each sequence.

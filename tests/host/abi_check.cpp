@@ -349,8 +349,9 @@ int main() {
 
   // ---- KV compaction: sizes whose products leave int64 must be refused, not wrap
   kv(131072, 256, 8, 64, SV_OK);
-  kv(int64_t(1) << 40, 1, 1, 1, SV_ERR_SHAPE);                   // 8 * 2^30 tiles
-  kv(int64_t(1) << 30, 1, 1, 1, SV_OK);
+  kv(int64_t(1) << 40, 1, 1, 1, SV_ERR_SHAPE);                   // 8 * 2^31 tiles
+  kv(int64_t(1) << 29, 1, 1, 1, SV_OK);                          // 8 * 2^20 tiles of 512 B
+  kv(int64_t(1) << 30, 1, 1, 1, SV_ERR_SHAPE);                   // 2^32 work-items
   kv((int64_t(1) << 40) + 1, 1, 1, 1, SV_ERR_SHAPE);
   kv(INT64_MAX, 1, 1, 1, SV_ERR_SHAPE);
   kv(int64_t(1) << 40, INT32_MAX, INT32_MAX, 1, SV_ERR_SHAPE);  // n * src_rows * row_bytes
