@@ -80,6 +80,18 @@ def test_gauss_b256_g7_v152064_full(gauss_b256):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_batch(dtype):
+    # 8192 sequences: grids of many workgroups on every path (the batch is past every
+    # one-workgroup gate, so the automatic choice would be the multi-kernel path); every
+    # sequence against the oracle.
+    b = I.chain_gaussian(29, 8192, 2, 64, dtype, 2.0, 1.0, np.linspace(0.3, 2.0, 8192))
+    counts = check_chain(b, run_chain(b))
+    report(f"large batch {dtype}", counts)
+    assert counts["fallback"] == 0
+    assert counts["exact"] + counts["accept_band"] + counts["edge_band"] == 8192
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [1, 2, 7, 63, 64, 65, 1000, 2047, 2048, 2049, 4100, 5003, 8191])
 def test_edge_shapes(dtype, V):
     for B, gamma, T in ((1, 1, 1.0), (3, 2, 0.5), (17, 7, 2.0)):

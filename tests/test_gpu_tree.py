@@ -61,6 +61,35 @@ def test_random_trees_with_ties(dtype, V, n_nodes):
     check_tree(b, run_tree(b))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_largest_tree_chain_shaped(dtype):
+    """Trees at the ABI's largest node count (4096): a chain of nodes where every node's argmax is
+    its child's token walks all 4095 drafts in tree 0 (the whole path and token arrays filled);
+    tree 1 stops at node 2000, tree 2 at the root."""
+    n, V = 4096, 7
+    rng = np.random.default_rng(4096)
+    parents = np.tile(np.arange(-1, n - 1, dtype=np.int32), (3, 1))
+    tokens = rng.integers(0, V, size=(3, n)).astype(np.int32)
+    z = np.zeros((3, n, V), dtype=np.float32)
+    for t in range(3):
+        for u in range(n - 1):
+            z[t, u, tokens[t, u + 1]] = 2.0
+    z[1, 2000, tokens[1, 2001]] = 0.0
+    z[1, 2000, (tokens[1, 2001] + 1) % V] = 3.0
+    z[2, 0, tokens[2, 1]] = -1.0
+    b = I.TreeBatch("chain4096", dtype, I.bf16_bits(z) if dtype == "bf16" else z, parents, tokens)
+    ks = check_tree(b, run_tree(b))
+    assert ks == [n - 1, 2000, 0]
+
+
+def test_largest_tree_random_two_chunks():
+    """4096-node random trees over two chunks per row (V = 2049) with frequent matches."""
+    b = I.tree_random(4097, 3, 4096, 2049, "bf16", boost=30.0, boost_prob=0.9, max_depth=64)
+    ks = check_tree(b, run_tree(b))
+    print(f"[parity] 4096-node trees accepted: {ks}", flush=True)
+    assert max(ks) >= 4
+
+
 def test_unaligned_and_signed_zero():
     b = I.tree_random(21, 4, 16, 4096, "bf16")
     z = I.bf16_value(b.logits).copy()
