@@ -21,8 +21,7 @@ order:
    to gamma+1 tokens per round, so a round that accepts all gamma drafts yields
    a (gamma+1)-th token).
 
-Readings of points the page leaves open (each is listed with its reason in the
-design notes of the repository):
+Readings of points the page leaves open:
 
 * Random numbers are inputs: uniforms[0:gamma] drive the accept tests and
   uniforms[gamma] drives the single draw (residual or bonus) by inverse CDF in
