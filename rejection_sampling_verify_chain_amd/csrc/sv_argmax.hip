@@ -90,15 +90,18 @@ __device__ __forceinline__ ArgPart argmax_chunk(const RawChunk<T, VW>& r) {
   return ArgPart{m, off, nan ? 1 : 0, 0};
 }
 
-// Workgroup size of the streaming argmax: as the softmax sweep's.
-template <typename T>
-constexpr int kArgBlock = kStreamBlock<T>;
+// Workgroup size of the streaming argmax: as the softmax sweep's, except 512 threads for two
+// chunks per wave (measured on the 16 x 64 x 32000 bf16 tree workload, about 1% ahead of 256
+// threads: 11.91-11.97 against 12.13-12.15 us on one box, 12.02-12.22 against 12.17-12.31 us on
+// another; 1024 threads 12.24-12.30 us; with one chunk per wave 256 stays best).
+template <typename T, int U>
+constexpr int kArgBlock = U == 2 ? 512 : kStreamBlock<T>;
 
 template <typename T, int VW, int U>
-__global__ __launch_bounds__(kArgBlock<T>, kStreamWavesPerSimd<VW>) void k_argmax_rows(
+__global__ __launch_bounds__((kArgBlock<T, U>), kStreamWavesPerSimd<VW>) void k_argmax_rows(
     const void* logits_v, int64_t V, int64_t nchunk, ArgPart* part, int64_t total) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t gw = int64_t(blockIdx.x) * (kArgBlock<T> / kWave) + wave_id();
+  const int64_t gw = int64_t(blockIdx.x) * (kArgBlock<T, U> / kWave) + wave_id();
   const T* logits = static_cast<const T*>(logits_v);
   stream_wave<RawChunk<T, VW>, U>(
       gw, total, nchunk, 1,
@@ -119,7 +122,6 @@ __global__ __launch_bounds__(kArgBlock<T>, kStreamWavesPerSimd<VW>) void k_argma
 // shorten the last round's tail.  Measured on bf16 rows: the 16 x 64 x 32000 tree workload
 // (16384 chunks, one round at two per wave) 12.6 -> 12.2 us; the 64 x 5 x 128256 greedy workload
 // (20160 chunks, 1.23 rounds at two per wave) 14.2 us at one chunk per wave against 15.1 at two.
-// 512- and 1024-thread workgroups were slower for both.
 int resident_waves(int waves_per_simd) {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cus[kMaxDevices];
@@ -139,16 +141,17 @@ hipError_t run(const char* name, const void* logits, int64_t rows, int64_t V, Ar
                hipStream_t s) {
   const int64_t nchunk = n_chunks(V);
   const int64_t total = rows * nchunk;
-  constexpr int wpb = kArgBlock<T> / kWave;
   const int64_t slots = resident_waves(kStreamWavesPerSimd<VW>);
   if constexpr (sizeof(T) == 2 && VW > 1) {  // 4 KiB chunks; an fp32 chunk is already 8 KiB
+    constexpr int wpb2 = kArgBlock<T, 2> / kWave;
     if (total > slots && total <= 2 * slots)
       return launch_kernel(name, k_argmax_rows<T, VW, 2>,
-                           dim3(unsigned(wave_groups(wave_groups(total, 2), wpb))),
-                           dim3(kArgBlock<T>), s, logits, V, nchunk, part, total);
+                           dim3(unsigned(wave_groups(wave_groups(total, 2), wpb2))),
+                           dim3(kArgBlock<T, 2>), s, logits, V, nchunk, part, total);
   }
+  constexpr int wpb = kArgBlock<T, 1> / kWave;
   return launch_kernel(name, k_argmax_rows<T, VW, 1>, dim3(unsigned(wave_groups(total, wpb))),
-                       dim3(kArgBlock<T>), s, logits, V, nchunk, part, total);
+                       dim3(kArgBlock<T, 1>), s, logits, V, nchunk, part, total);
 }
 
 }  // namespace
