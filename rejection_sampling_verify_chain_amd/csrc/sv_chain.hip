@@ -314,11 +314,20 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
     const LazyForm form =
         a.lazy ? lazy_form(a, L.nchunk, kStageUnits<T>, sizeof(T)) : LazyForm::kNone;
     if (form == LazyForm::kStaged) {
-      for (int j = 0; j <= a.gamma + 1; ++j) {
+      const int tail = stage_tail(a.gamma);
+      for (int j = 0; j <= a.gamma + 1 && j <= tail; ++j) {
         const int G = stage_groups(j, a.gamma, L.nchunk, kStageUnits<T>);
-        const hipError_t e = launch_kernel("chain_stage", k_chain_stage<T, VW>,
-                                           dim3(unsigned(int64_t(a.B) * G)),
-                                           dim3(kStageBlock), s, p, j, G);
+        const dim3 grid(unsigned(int64_t(a.B) * G));
+        const hipError_t e =
+            j == tail ? launch_kernel("chain_stage", k_chain_stage<T, VW, true>, grid,
+                                      dim3(kStageBlock), s, p, j, G)
+                      : launch_kernel("chain_stage", k_chain_stage<T, VW, false>, grid,
+                                      dim3(kStageBlock), s, p, j, G);
+        if (e != hipSuccess) return e;
+      }
+      if (tail <= a.gamma) {
+        const hipError_t e = launch_kernel("chain_stage_rest", k_chain_stage_rest<T, VW>,
+                                           dim3(unsigned(a.B)), dim3(kStageBlock), s, p, tail);
         if (e != hipSuccess) return e;
       }
       const int64_t rtotal = int64_t(a.B) * L.nchunk;

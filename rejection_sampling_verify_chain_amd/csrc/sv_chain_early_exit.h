@@ -219,8 +219,13 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_lazy(ChainParams p) {
 // decision and row statistics.  After an accept the workgroup sweeps its slice of row pair j
 // (target row gamma alone at j = gamma) into chunk partials and fetches the drafted token's two
 // logits at position j; otherwise it exits.  Launch 0 sweeps pair 0 of every sequence and checks
-// the inputs that need no logit row.  The multi-kernel path's residual and draw kernels then
-// finish every sequence from the decisions.  Rows after the cut are never read, and each step
+// the inputs that need no logit row.  Few sequences are left after the first positions, and a
+// launch that sweeps one pair for them is mostly fixed cost, so from position kStageTailFrom on
+// (when gamma > kStageTailFrom) launch kStageTailFrom sweeps every remaining row of the sequences
+// still alive (pairs kStageTailFrom .. gamma - 1 and the bonus row) and one more launch,
+// chain_stage_rest, decides those positions in order, one workgroup per sequence.  The
+// multi-kernel path's residual and draw kernels then finish every sequence from the decisions.
+// Rows after the cut are read only by that last sweep and never change a result, and each step
 // calls the eager path's device functions on the same values, so the outputs agree with
 // sv_verify_chain bit for bit (p and q after the cut excepted).
 
@@ -228,6 +233,16 @@ enum StageRole : int32_t { kStageExit = 0, kStageSweep = 1 };
 
 constexpr int kStageBlock = 256;
 constexpr int kStageWavesPerSimd = 8;
+// First position whose launch sweeps all the remaining rows (see above); that launch keeps two
+// chunks per wave in flight, at the occupancy their registers allow.
+// Measured on 256 sequences of gamma = 7, V = 152064 fp32 (mean accepted 0.56) per call: one
+// launch per position 187.6-188.0 us; all remaining rows from position 3 on 182.3-183.3 us, from
+// position 2 on 191.9-192.6 us, from position 4 on 185.2-185.4 us.
+constexpr int kStageTailFrom = 3;
+constexpr int kStageTailWavesPerSimd = 4;
+
+// The launch that sweeps all remaining rows, or gamma + 2 (none) for short drafts.
+inline int stage_tail(int gamma) { return gamma > kStageTailFrom ? kStageTailFrom : gamma + 2; }
 template <typename T>
 constexpr int kStageUnits = (kStageBlock / kWave) * kUnitsPerWave<T>;  // chunks per workgroup
 
@@ -238,9 +253,81 @@ inline int stage_groups(int j, int gamma, int64_t nchunk, int units_per_group) {
   return int((units + units_per_group - 1) / units_per_group);
 }
 
-template <typename T, int VW>
-__global__ __launch_bounds__(kStageBlock, kStageWavesPerSimd) void k_chain_stage(
-    ChainParams p, int j, int G) {
+// Decision of position i of sequence b (i == gamma: the bonus row) from the merged statistics of
+// target row i (a) and draft row i (d), with the drafted token's logits fetched earlier into lz
+// (one wave; the eager path's arithmetic).  lead: write the outputs, and at a cut or the bonus row
+// the decision and row statistics.  Returns whether the sequence goes on to position i + 1.
+__device__ bool stage_decide(const ChainParams& p, int64_t b, int i, const RowStat& a,
+                             const RowStat& d, int status, double Td, bool lead, int lane) {
+  const int gamma = p.gamma;
+  const int R = 2 * gamma + 1;
+  if (!a.valid || !d.valid) status |= SV_ROW_NONFINITE;
+  if (status != 0) {
+    if (lead) {
+      write_fallback(p, b, status, lane);
+      if (lane == 0) p.seq[b] = SeqDecision{0, kDrawNone, status, 0};
+    }
+    return false;
+  }
+  if (i == gamma) {
+    if (lead && lane == 0) {
+      p.rowstat[b * R + gamma] = a;
+      p.seq[b] = SeqDecision{gamma, kDrawBonus, 0, 0};
+    }
+    return false;
+  }
+  const int x = uniform_load(p.toks, b * gamma + i);
+  const float zt = uniform_load(p.lz, (b * gamma + i) * 2);
+  const float zd = uniform_load(p.lz, (b * gamma + i) * 2 + 1);
+  const double pi = exp((double(zt) - double(a.m)) / Td) / a.s;
+  const double qi = exp((double(zd) - double(d.m)) / Td) / d.s;
+  const double u = uniform_load(p.uni, b * (gamma + 1) + i);
+  const bool accept = qi > 0.0 ? u < fmin(1.0, pi / qi) : (pi > 0.0) && (u < 1.0);
+  if (lead) {
+    if (lane == 0) {
+      if (p.out_p) p.out_p[b * gamma + i] = float(pi);
+      if (p.out_q) p.out_q[b * gamma + i] = float(qi);
+    }
+    if (accept) {
+      if (lane == 0) p.out_tokens[b * (gamma + 1) + i] = x;
+    } else {
+      // The cut: padding, and positions never evaluated (p, q NaN).
+      for (int t = i + 1 + lane; t <= gamma; t += kWave) {
+        p.out_tokens[b * (gamma + 1) + t] = -1;
+        if (t < gamma && p.out_p) p.out_p[b * gamma + t] = NAN;
+        if (t < gamma && p.out_q) p.out_q[b * gamma + t] = NAN;
+      }
+      if (lane == 0) {
+        p.rowstat[b * R + i] = a;
+        p.rowstat[b * R + gamma + 1 + i] = d;
+        p.seq[b] = SeqDecision{i, kDrawResidual, 0, 0};
+      }
+    }
+  }
+  return accept;
+}
+
+// The drafted tokens' two logits at positions i = i0 + lane, i0 + lane + 64, ... < i1 (one wave),
+// for the decisions of those positions.
+template <typename T>
+__device__ __forceinline__ void fetch_drafted(const ChainParams& p, int64_t b, int i0, int i1,
+                                              int lane) {
+  const T* tgt = static_cast<const T*>(p.tgt);
+  const T* drf = static_cast<const T*>(p.drf);
+  for (int i = i0 + lane; i < i1; i += kWave) {
+    const int x = p.toks[b * p.gamma + i];
+    if (x >= 0 && int64_t(x) < p.V) {
+      p.lz[(b * p.gamma + i) * 2] = widen(chain_row(tgt, drf, b, p.gamma, i, p.V)[x]);
+      p.lz[(b * p.gamma + i) * 2 + 1] =
+          widen(chain_row(tgt, drf, b, p.gamma, p.gamma + 1 + i, p.V)[x]);
+    }
+  }
+}
+
+template <typename T, int VW, bool TAIL>
+__global__ __launch_bounds__(kStageBlock, TAIL ? kStageTailWavesPerSimd : kStageWavesPerSimd) void
+k_chain_stage(ChainParams p, int j, int G) {
+  constexpr bool tail = TAIL;
   __shared__ RowStat st2[2];
   __shared__ int32_t role;
   const int64_t b = blockIdx.x / G;
@@ -296,51 +383,8 @@ __global__ __launch_bounds__(kStageBlock, kStageWavesPerSimd) void k_chain_stage
     if (wave == 0) {
       const RowStat a = st2[0];
       const RowStat d = i < gamma ? st2[1] : a;
-      int status = i == 0 ? uniform_load(p.hstat, b) : 0;
-      if (!a.valid || !d.valid) status |= SV_ROW_NONFINITE;
-      int rr = kStageExit;
-      if (status != 0) {
-        if (lead) {
-          write_fallback(p, b, status, lane);
-          if (lane == 0) p.seq[b] = SeqDecision{0, kDrawNone, status, 0};
-        }
-      } else if (i == gamma) {
-        if (lead && lane == 0) {
-          p.rowstat[b * R + gamma] = a;
-          p.seq[b] = SeqDecision{gamma, kDrawBonus, 0, 0};
-        }
-      } else {
-        // Position i's test on the logits launch i fetched (the eager path's arithmetic).
-        const int x = uniform_load(p.toks, b * gamma + i);
-        const float zt = uniform_load(p.lz, (b * gamma + i) * 2);
-        const float zd = uniform_load(p.lz, (b * gamma + i) * 2 + 1);
-        const double pi = exp((double(zt) - double(a.m)) / Td) / a.s;
-        const double qi = exp((double(zd) - double(d.m)) / Td) / d.s;
-        const double u = uniform_load(p.uni, b * (gamma + 1) + i);
-        const bool accept = qi > 0.0 ? u < fmin(1.0, pi / qi) : (pi > 0.0) && (u < 1.0);
-        if (lead) {
-          if (lane == 0) {
-            if (p.out_p) p.out_p[b * gamma + i] = float(pi);
-            if (p.out_q) p.out_q[b * gamma + i] = float(qi);
-          }
-          if (accept) {
-            if (lane == 0) p.out_tokens[b * (gamma + 1) + i] = x;
-          } else {
-            // The cut: padding, and positions never evaluated (p, q NaN).
-            for (int t = i + 1 + lane; t <= gamma; t += kWave) {
-              p.out_tokens[b * (gamma + 1) + t] = -1;
-              if (t < gamma && p.out_p) p.out_p[b * gamma + t] = NAN;
-              if (t < gamma && p.out_q) p.out_q[b * gamma + t] = NAN;
-            }
-            if (lane == 0) {
-              p.rowstat[b * R + i] = a;
-              p.rowstat[b * R + gamma + 1 + i] = d;
-              p.seq[b] = SeqDecision{i, kDrawResidual, 0, 0};
-            }
-          }
-        }
-        rr = accept ? kStageSweep : kStageExit;
-      }
+      const int status = i == 0 ? uniform_load(p.hstat, b) : 0;
+      const int rr = stage_decide(p, b, i, a, d, status, Td, lead, lane) ? kStageSweep : kStageExit;
       if (lead && lane == 0) p.alive[b * 2 + (j & 1)] = rr == kStageSweep ? 1 : 0;
       if (lane == 0) role = rr;
     }
@@ -350,15 +394,51 @@ __global__ __launch_bounds__(kStageBlock, kStageWavesPerSimd) void k_chain_stage
 
   constexpr int U = kUnitsPerWave<T>;
   const int64_t u0 = int64_t(g) * kStageUnits<T> + int64_t(wave) * U;
-  if (r == kStageSweep) {
-    if (lead && wave == 0 && j < gamma) {
-      // The drafted token's logits at position j, for launch j + 1's test.
-      const int x = uniform_load(p.toks, b * gamma + j);
-      if (lane == 0 && x >= 0 && int64_t(x) < p.V) {
-        p.lz[(b * gamma + j) * 2] = widen(chain_row(tgt, drf, b, gamma, j, p.V)[x]);
-        p.lz[(b * gamma + j) * 2 + 1] = widen(chain_row(tgt, drf, b, gamma, gamma + 1 + j, p.V)[x]);
+  if (r == kStageSweep && tail) {
+    // Every remaining row: pairs j .. gamma - 1, then the bonus row, G workgroups striding over
+    // their chunks; the drafted tokens' logits of positions j .. gamma - 1.
+    static_assert(U == 1, "the remaining rows are taken one chunk per wave at a time");
+    if (lead && wave == 0) fetch_drafted<T>(p, b, j, gamma, lane);
+    const int64_t pair_units = int64_t(gamma - j) * 2 * nchunk;
+    const int64_t units = pair_units + nchunk;
+    const int64_t stride = int64_t(G) * kStageUnits<T>;
+    auto where = [&](int64_t w, int& row, int64_t& c) {
+      if (w < pair_units) {
+        const int64_t q = w / (2 * nchunk), rem = w - q * 2 * nchunk;
+        row = rem < nchunk ? j + int(q) : gamma + 1 + j + int(q);
+        c = rem < nchunk ? rem : rem - nchunk;
+      } else {
+        row = gamma;
+        c = w - pair_units;
+      }
+    };
+    // Two chunks per wave in flight: the next one's loads go out before this one is reduced.
+    for (int64_t w = u0; w < units; w += 2 * stride) {  // wave-uniform
+      int row0, row1;
+      int64_t c0, c1;
+      const int64_t w1 = w + stride < units ? w + stride : w;  // the last odd one reloads w
+      where(w, row0, c0);
+      where(w1, row1, c1);
+      RawChunk<T, VW> r0, r1;
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, row0, p.V) + c0 * kChunk,
+                      chunk_valid(p.V, c0), lane, r0);
+      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, row1, p.V) + c1 * kChunk,
+                      chunk_valid(p.V, c1), lane, r1);
+      float z[kElemsPerLane];
+      unpack_chunk<T, VW>(r0, chunk_valid(p.V, c0), lane, z);
+      RowPart rp = reduce_chunk(z, kk);
+      if (lane == 0) p.part[(b * R + row0) * nchunk + c0] = rp;
+      if (w1 != w) {
+        unpack_chunk<T, VW>(r1, chunk_valid(p.V, c1), lane, z);
+        rp = reduce_chunk(z, kk);
+        if (lane == 0) p.part[(b * R + row1) * nchunk + c1] = rp;
       }
     }
+    return;
+  }
+  if (r == kStageSweep) {
+    // The drafted token's logits at position j, for launch j + 1's test.
+    if (lead && wave == 0 && j < gamma) fetch_drafted<T>(p, b, j, j + 1, lane);
     const int64_t units = (j < gamma ? 2 : 1) * nchunk;
     RawChunk<T, VW> raw[U];
 #pragma unroll
@@ -381,6 +461,35 @@ __global__ __launch_bounds__(kStageBlock, kStageWavesPerSimd) void k_chain_stage
         if (lane == 0) p.part[(b * R + row) * nchunk + c] = rp;
       }
     }
+  }
+}
+
+// Positions s .. gamma - 1 and the bonus row of the sequences that reached position s, in order,
+// after launch s swept all their remaining rows (one 256-thread workgroup per sequence): the
+// rows' partials are merged, a wave per row, then one wave takes the decisions.
+template <typename T, int VW>
+__global__ __launch_bounds__(kStageBlock) void k_chain_stage_rest(ChainParams p, int s) {
+  __shared__ RowStat st[2 * kMaxGamma + 1];
+  const int64_t b = blockIdx.x;
+  if (!uniform_load(p.alive, b * 2 + (s & 1))) return;  // the whole workgroup
+  const int gamma = p.gamma;
+  const int R = 2 * gamma + 1;
+  const int npos = gamma - s;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & (kWave - 1);
+  const double Td = effective_temperature(uniform_load(p.temp, b));
+  // Merged row q: target row s + q (q < npos), draft row s + q - npos (q < 2 npos), the bonus row.
+  for (int q = wave; q < 2 * npos + 1; q += kStageBlock / kWave) {
+    const int row = q < npos ? s + q : q < 2 * npos ? gamma + 1 + s + (q - npos) : gamma;
+    const RowStat rs = merge_row(p.part + (b * R + row) * p.nchunk, p.nchunk, lane, Td);
+    if (lane == 0) st[q] = rs;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  for (int i = s; i <= gamma; ++i) {  // wave-uniform
+    const RowStat a = i < gamma ? st[i - s] : st[2 * npos];
+    const RowStat d = i < gamma ? st[npos + i - s] : a;
+    if (!stage_decide(p, b, i, a, d, 0, Td, true, lane)) break;
   }
 }
 
