@@ -397,7 +397,7 @@ k_chain_stage(ChainParams p, int j, int G) {
   if (r == kStageSweep && tail) {
     // Every remaining row: pairs j .. gamma - 1, then the bonus row, G workgroups striding over
     // their chunks; the drafted tokens' logits of positions j .. gamma - 1.
-    static_assert(U == 1, "the remaining rows are taken one chunk per wave at a time");
+    static_assert(U == 1, "the stride below gives each wave one unit per step");
     if (lead && wave == 0) fetch_drafted<T>(p, b, j, gamma, lane);
     const int64_t pair_units = int64_t(gamma - j) * 2 * nchunk;
     const int64_t units = pair_units + nchunk;
