@@ -327,7 +327,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
       }
       if (tail <= a.gamma) {
         const hipError_t e = launch_kernel("chain_stage_rest", k_chain_stage_rest<T, VW>,
-                                           dim3(unsigned(a.B)), dim3(kStageBlock), s, p, tail);
+                                           dim3(unsigned(a.B)), dim3(kStageRestBlock), s, p, tail);
         if (e != hipSuccess) return e;
       }
       const int64_t rtotal = int64_t(a.B) * L.nchunk;

@@ -465,10 +465,13 @@ k_chain_stage(ChainParams p, int j, int G) {
 }
 
 // Positions s .. gamma - 1 and the bonus row of the sequences that reached position s, in order,
-// after launch s swept all their remaining rows (one 256-thread workgroup per sequence): the
-// rows' partials are merged, a wave per row, then one wave takes the decisions.
+// after launch s swept all their remaining rows (one 1024-thread workgroup per sequence): the
+// rows' partials are merged, a wave per row, then one wave takes the decisions.  Measured on 256
+// sequences of gamma = 7, V = 152064 fp32: 5.5 us against 6.7-6.9 us with 256 threads (the nine
+// merges of gamma - 3 pairs and the bonus row in one round of waves instead of three).
+constexpr int kStageRestBlock = 1024;
 template <typename T, int VW>
-__global__ __launch_bounds__(kStageBlock) void k_chain_stage_rest(ChainParams p, int s) {
+__global__ __launch_bounds__(kStageRestBlock) void k_chain_stage_rest(ChainParams p, int s) {
   __shared__ RowStat st[2 * kMaxGamma + 1];
   const int64_t b = blockIdx.x;
   if (!uniform_load(p.alive, b * 2 + (s & 1))) return;  // the whole workgroup
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(kStageBlock) void k_chain_stage_rest(ChainParams p,
   const int lane = threadIdx.x & (kWave - 1);
   const double Td = effective_temperature(uniform_load(p.temp, b));
   // Merged row q: target row s + q (q < npos), draft row s + q - npos (q < 2 npos), the bonus row.
-  for (int q = wave; q < 2 * npos + 1; q += kStageBlock / kWave) {
+  for (int q = wave; q < 2 * npos + 1; q += kStageRestBlock / kWave) {
     const int row = q < npos ? s + q : q < 2 * npos ? gamma + 1 + s + (q - npos) : gamma;
     const RowStat rs = merge_row(p.part + (b * R + row) * p.nchunk, p.nchunk, lane, Td);
     if (lane == 0) st[q] = rs;
