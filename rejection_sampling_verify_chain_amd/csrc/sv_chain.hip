@@ -303,7 +303,9 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   p.out_p = a.out_p;
   p.out_q = a.out_q;
   p.out_status = a.out_status;
-  p.alive = reinterpret_cast<int32_t*>(a.ws + L.off_alive);
+  p.B = a.B;
+  p.live_count = reinterpret_cast<int32_t*>(a.ws + L.off_live);
+  p.live = p.live_count + kStageCountPad;
   p.hstat = reinterpret_cast<int32_t*>(a.ws + L.off_hstat);
   p.lz = reinterpret_cast<float*>(a.ws + L.off_lz);
 
@@ -315,14 +317,17 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
         a.lazy ? lazy_form(a, L.nchunk, kStageUnits<T>, sizeof(T)) : LazyForm::kNone;
     if (form == LazyForm::kStaged) {
       const int tail = stage_tail(a.gamma);
-      for (int j = 0; j <= a.gamma + 1 && j <= tail; ++j) {
+      for (int j = 0; j <= a.gamma && j <= tail; ++j) {
         const int G = stage_groups(j, a.gamma, L.nchunk, kStageUnits<T>);
         const dim3 grid(unsigned(int64_t(a.B) * G));
-        const hipError_t e =
-            j == tail ? launch_kernel("chain_stage", k_chain_stage<T, VW, true>, grid,
-                                      dim3(kStageBlock), s, p, j, G)
-                      : launch_kernel("chain_stage", k_chain_stage<T, VW, false>, grid,
-                                      dim3(kStageBlock), s, p, j, G);
+        hipError_t e = j == tail ? launch_kernel("chain_stage", k_chain_stage<T, VW, true>, grid,
+                                                 dim3(kStageBlock), s, p, j, G)
+                                 : launch_kernel("chain_stage", k_chain_stage<T, VW, false>, grid,
+                                                 dim3(kStageBlock), s, p, j, G);
+        if (e != hipSuccess) return e;
+        if (j == tail) break;
+        e = launch_kernel("chain_stage_decide", k_chain_stage_decide, dim3(unsigned(a.B)),
+                          dim3(kStageDecideBlock), s, p, j);
         if (e != hipSuccess) return e;
       }
       if (tail <= a.gamma) {

@@ -36,10 +36,12 @@ struct ChainParams {
   float* out_p;
   float* out_q;
   int32_t* out_status;
-  // Staged early exit only: per sequence, "reached position j" flags [B][2] (slot j & 1), the
-  // checks that need no logit row [B], and the drafted tokens' target and draft logits
-  // [B][gamma][2].
-  int32_t* alive = nullptr;
+  // Staged early exit only: the batch size; list t of the sequences that reached position t + 1
+  // (live + t * B, live_count[t] entries, in no fixed order); the checks that need no logit row
+  // [B]; and the drafted tokens' target and draft logits [B][gamma][2].
+  int64_t B = 0;
+  int32_t* live_count = nullptr;
+  int32_t* live = nullptr;
   int32_t* hstat = nullptr;
   float* lz = nullptr;
 };

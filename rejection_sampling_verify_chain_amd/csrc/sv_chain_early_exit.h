@@ -211,25 +211,24 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_lazy(ChainParams p) {
 
 // ------------------------------------------------------------------------ early exit, staged
 //
-// The positions in order with the whole chip on each: launch j (0 <= j <= gamma + 1) works on
-// every sequence that reached position j - 1, in workgroups that each take a slice of its
-// chunks.  Every workgroup first decides position j - 1 itself (waves 0 and 1 merge the chunk
-// partials of target and draft row j - 1; at j = gamma + 1 only target row gamma, the bonus
-// row), and workgroup 0 writes the sequence's outputs and, at a cut or the bonus row, the
-// decision and row statistics.  After an accept the workgroup sweeps its slice of row pair j
-// (target row gamma alone at j = gamma) into chunk partials and fetches the drafted token's two
-// logits at position j; otherwise it exits.  Launch 0 sweeps pair 0 of every sequence and checks
-// the inputs that need no logit row.  Few sequences are left after the first positions, and a
-// launch that sweeps one pair for them is mostly fixed cost, so from position kStageTailFrom on
-// (when gamma > kStageTailFrom) launch kStageTailFrom sweeps every remaining row of the sequences
-// still alive (pairs kStageTailFrom .. gamma - 1 and the bonus row) and one more launch,
-// chain_stage_rest, decides those positions in order, one workgroup per sequence.  The
+// The positions in order with the whole chip on each.  For position j a sweep launch
+// (chain_stage) streams row pair j (target row gamma alone at j = gamma, the bonus row) of every
+// sequence that reached position j into chunk partials, in workgroups that each take a slice of
+// its chunks, and fetches the drafted token's two logits at j; then a decision launch
+// (chain_stage_decide, one workgroup per sequence) merges the pair's partials, tests position j,
+// writes the outputs and, at a cut or the bonus row, the decision and row statistics.  The
+// sequences that accept join a list in the workspace (an atomic add per sequence), and the next
+// sweep and decision take that list: their grids cover the whole batch, the leading workgroups
+// take the listed sequences and the rest exit at once.  Launch 0 also checks the inputs that need
+// no logit row.  Few sequences are left after the first positions, and a launch that sweeps one
+// pair for them is mostly fixed cost, so from position kStageTailFrom on (when gamma >
+// kStageTailFrom) one sweep launch takes every remaining row of the sequences still in (pairs
+// kStageTailFrom .. gamma - 1 and the bonus row) and one more launch, chain_stage_rest, decides
+// those positions in order, one workgroup per sequence.  The
 // multi-kernel path's residual and draw kernels then finish every sequence from the decisions.
 // Rows after the cut are read only by that last sweep and never change a result, and each step
 // calls the eager path's device functions on the same values, so the outputs agree with
 // sv_verify_chain bit for bit (p and q after the cut excepted).
-
-enum StageRole : int32_t { kStageExit = 0, kStageSweep = 1 };
 
 constexpr int kStageBlock = 256;
 constexpr int kStageWavesPerSimd = 8;
@@ -240,6 +239,8 @@ constexpr int kStageWavesPerSimd = 8;
 // position 2 on 191.9-192.6 us, from position 4 on 185.2-185.4 us.
 constexpr int kStageTailFrom = 3;
 constexpr int kStageTailWavesPerSimd = 4;
+static_assert(kStageTailFrom <= kStageLists,
+              "launches 2 .. kStageTailFrom and the last step each read a list of the workspace");
 
 // The launch that sweeps all remaining rows, or gamma + 2 (none) for short drafts.
 inline int stage_tail(int gamma) { return gamma > kStageTailFrom ? kStageTailFrom : gamma + 2; }
@@ -324,15 +325,24 @@ __device__ __forceinline__ void fetch_drafted(const ChainParams& p, int64_t b, i
   }
 }
 
+// Sweep launch j: pair j (target row gamma alone at j = gamma) of every sequence that reached
+// position j, or with TAIL every row it still has (pairs j .. gamma - 1 and the bonus row), in
+// G workgroups per sequence.  Launch 0 takes every sequence, checks the inputs that need no logit
+// row and empties the lists; launch j > 0 takes list j - 1, its leading workgroups working and
+// those past the list's end exiting at once.  The lead workgroup also fetches the drafted
+// tokens' two logits at the positions it sweeps, for their decisions.
 template <typename T, int VW, bool TAIL>
 __global__ __launch_bounds__(kStageBlock, TAIL ? kStageTailWavesPerSimd : kStageWavesPerSimd) void
 k_chain_stage(ChainParams p, int j, int G) {
-  constexpr bool tail = TAIL;
-  __shared__ RowStat st2[2];
-  __shared__ int32_t role;
-  const int64_t b = blockIdx.x / G;
-  const int g = int(blockIdx.x - b * G);
-  const bool lead = g == 0;  // writes the sequence's outputs
+  const int64_t rank = blockIdx.x / G;
+  const int g = int(blockIdx.x - rank * G);
+  int64_t b = rank;
+  if (j >= 1) {
+    const int32_t listed = uniform_load(p.live, (j - 1) * p.B + rank);  // rank < B: in the list
+    if (rank >= uniform_load(p.live_count, j - 1)) return;  // the whole workgroup
+    b = listed;
+  }
+  const bool lead = g == 0;
   const int gamma = p.gamma;
   const int R = 2 * gamma + 1;
   const int64_t nchunk = p.nchunk;
@@ -341,14 +351,11 @@ k_chain_stage(ChainParams p, int j, int G) {
   const T* tgt = static_cast<const T*>(p.tgt);
   const T* drf = static_cast<const T*>(p.drf);
   const float tb = uniform_load(p.temp, b);
-  const float te = effective_temperature(tb);
-  const double Td = te;
-  const float kk = log2e_over_t(te);
+  const float kk = log2e_over_t(effective_temperature(tb));
 
-  int r = kStageSweep;
   if (j == 0) {
     if (lead && wave == 0) {
-      // Checks that read no logit row; launch 1 takes the fallback on them.
+      // Checks that read no logit row; the decision of position 0 takes the fallback on them.
       int status = 0;
       if (!(tb > 0.0f && tb < INFINITY)) status |= SV_ROW_BAD_TEMPERATURE;
       bool bad = false;
@@ -363,38 +370,15 @@ k_chain_stage(ChainParams p, int j, int G) {
         bad |= (x < 0) || (int64_t(x) >= p.V);
       }
       if (__any(bad)) status |= SV_ROW_TOKEN_RANGE;
-      if (lane == 0) {
-        p.hstat[b] = status;
-        p.alive[b * 2] = 1;
-      }
+      if (lane == 0) p.hstat[b] = status;
     }
-  } else {
-    const int i = j - 1;  // the position decided here; i == gamma: the bonus row
-    if (!uniform_load(p.alive, b * 2 + (i & 1))) {
-      if (lead && threadIdx.x == 0) p.alive[b * 2 + (j & 1)] = 0;
-      return;  // the whole workgroup: the flag is uniform
-    }
-    if (wave < (i < gamma ? 2 : 1)) {
-      const RowStat st = merge_row(p.part + (b * R + (wave == 0 ? i : gamma + 1 + i)) * nchunk,
-                                   nchunk, lane, Td);
-      if (lane == 0) st2[wave] = st;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const RowStat a = st2[0];
-      const RowStat d = i < gamma ? st2[1] : a;
-      const int status = i == 0 ? uniform_load(p.hstat, b) : 0;
-      const int rr = stage_decide(p, b, i, a, d, status, Td, lead, lane) ? kStageSweep : kStageExit;
-      if (lead && lane == 0) p.alive[b * 2 + (j & 1)] = rr == kStageSweep ? 1 : 0;
-      if (lane == 0) role = rr;
-    }
-    __syncthreads();
-    r = role;
+    if (blockIdx.x == 0 && threadIdx.x == 0)  // the lists start empty each call
+      for (int t = 0; t < kStageLists; ++t) p.live_count[t] = 0;
   }
 
   constexpr int U = kUnitsPerWave<T>;
   const int64_t u0 = int64_t(g) * kStageUnits<T> + int64_t(wave) * U;
-  if (r == kStageSweep && tail) {
+  if (TAIL) {
     // Every remaining row: pairs j .. gamma - 1, then the bonus row, G workgroups striding over
     // their chunks; the drafted tokens' logits of positions j .. gamma - 1.
     static_assert(U == 1, "the stride below gives each wave one unit per step");
@@ -436,31 +420,66 @@ k_chain_stage(ChainParams p, int j, int G) {
     }
     return;
   }
-  if (r == kStageSweep) {
-    // The drafted token's logits at position j, for launch j + 1's test.
-    if (lead && wave == 0 && j < gamma) fetch_drafted<T>(p, b, j, j + 1, lane);
-    const int64_t units = (j < gamma ? 2 : 1) * nchunk;
-    RawChunk<T, VW> raw[U];
+  // The drafted token's logits at position j, for its decision.
+  if (lead && wave == 0 && j < gamma) fetch_drafted<T>(p, b, j, j + 1, lane);
+  const int64_t units = (j < gamma ? 2 : 1) * nchunk;
+  RawChunk<T, VW> raw[U];
 #pragma unroll
-    for (int t = 0; t < U; ++t) {
-      const int64_t w = min(u0 + t, units - 1);
+  for (int t = 0; t < U; ++t) {
+    const int64_t w = min(u0 + t, units - 1);
+    const int row = w < nchunk ? j : gamma + 1 + j;
+    const int64_t c = w < nchunk ? w : w - nchunk;
+    load_raw<T, VW>(chain_row(tgt, drf, b, gamma, row, p.V) + c * kChunk, chunk_valid(p.V, c),
+                    lane, raw[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < U; ++t) {
+    const int64_t w = u0 + t;
+    if (w < units) {  // wave-uniform
       const int row = w < nchunk ? j : gamma + 1 + j;
       const int64_t c = w < nchunk ? w : w - nchunk;
-      load_raw<T, VW>(chain_row(tgt, drf, b, gamma, row, p.V) + c * kChunk, chunk_valid(p.V, c),
-                      lane, raw[t]);
+      float z[kElemsPerLane];
+      unpack_chunk<T, VW>(raw[t], chunk_valid(p.V, c), lane, z);
+      const RowPart rp = reduce_chunk(z, kk);
+      if (lane == 0) p.part[(b * R + row) * nchunk + c] = rp;
     }
-#pragma unroll
-    for (int t = 0; t < U; ++t) {
-      const int64_t w = u0 + t;
-      if (w < units) {  // wave-uniform
-        const int row = w < nchunk ? j : gamma + 1 + j;
-        const int64_t c = w < nchunk ? w : w - nchunk;
-        float z[kElemsPerLane];
-        unpack_chunk<T, VW>(raw[t], chunk_valid(p.V, c), lane, z);
-        const RowPart rp = reduce_chunk(z, kk);
-        if (lane == 0) p.part[(b * R + row) * nchunk + c] = rp;
-      }
-    }
+  }
+}
+
+// Decision of position i (i == gamma: the bonus row) for every sequence that reached it (all at
+// i = 0, else list i - 1), one workgroup each: waves 0 and 1 merge the chunk partials of target
+// row i and draft row i, and wave 0 decides and writes the outputs.  A sequence that accepts
+// (i < gamma) joins list i, which the next sweep launch and decision take.
+constexpr int kStageDecideBlock = 2 * kWave;
+__global__ __launch_bounds__(kStageDecideBlock) void k_chain_stage_decide(ChainParams p, int i) {
+  __shared__ RowStat st2[2];
+  const int64_t rank = blockIdx.x;
+  int64_t b = rank;
+  if (i >= 1) {
+    const int32_t listed = uniform_load(p.live, (i - 1) * p.B + rank);  // rank < B: in the list
+    if (rank >= uniform_load(p.live_count, i - 1)) return;  // the whole workgroup
+    b = listed;
+  }
+  const int gamma = p.gamma;
+  const int R = 2 * gamma + 1;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & (kWave - 1);
+  const double Td = effective_temperature(uniform_load(p.temp, b));
+  if (wave < (i < gamma ? 2 : 1)) {
+    const RowStat st = merge_row(p.part + (b * R + (wave == 0 ? i : gamma + 1 + i)) * p.nchunk,
+                                 p.nchunk, lane, Td);
+    if (lane == 0) st2[wave] = st;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const RowStat a = st2[0];
+  const RowStat d = i < gamma ? st2[1] : a;
+  const int status = i == 0 ? uniform_load(p.hstat, b) : 0;
+  if (stage_decide(p, b, i, a, d, status, Td, true, lane) && lane == 0 && i < kStageLists) {
+    // Reached position i + 1: list i.
+    const int32_t at = __hip_atomic_fetch_add(&p.live_count[i], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    p.live[i * p.B + at] = int32_t(b);
   }
 }
 
@@ -473,8 +492,11 @@ constexpr int kStageRestBlock = 1024;
 template <typename T, int VW>
 __global__ __launch_bounds__(kStageRestBlock) void k_chain_stage_rest(ChainParams p, int s) {
   __shared__ RowStat st[2 * kMaxGamma + 1];
-  const int64_t b = blockIdx.x;
-  if (!uniform_load(p.alive, b * 2 + (s & 1))) return;  // the whole workgroup
+  // The rank-th sequence that reached position s (listed by launch s); the rest of the grid exits.
+  const int64_t rank = blockIdx.x;
+  const int32_t listed = uniform_load(p.live, (s - 1) * p.B + rank);  // rank < B: in the list
+  if (rank >= uniform_load(p.live_count, s - 1)) return;  // the whole workgroup
+  const int64_t b = listed;
   const int gamma = p.gamma;
   const int R = 2 * gamma + 1;
   const int npos = gamma - s;
