@@ -65,15 +65,24 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(ChainParams p) {
 // The wave's chunk loads of both rows are issued as soon as the decision (which row) is known;
 // the chunk partials and row statistics that scale them arrive through the scalar cache while
 // the chunk is in flight.  A chunk whose target part is all -inf (A = 0) is loaded too and adds
-// nothing.
+// nothing.  pending (staged early exit, else -1): a sequence that reached this position in the
+// last sweep has no decision yet; each of its waves takes the decisions from the chunk partials
+// itself (finish_pending; the chunk-0 wave writes them), with the cut pair's statistics in hand.
 template <typename T, int VW>
-__global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p, int64_t total) {
+__global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p, int64_t total,
+                                                                   int pending) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t w = int64_t(blockIdx.x) * (kResidualBlock / kWave) + wave_id();
   if (w >= total) return;  // wave-uniform
   const int64_t b = w / p.nchunk;
   const int64_t c = w - b * p.nchunk;
-  const SeqDecision d = uniform_load(p.seq, b);
+  const bool decide_here = pending >= 0 && uniform_load(p.reached, b) == pending;
+  RowStat st_t{}, st_d{};
+  SeqDecision d;
+  if (decide_here)
+    d = finish_pending(p, b, pending, c == 0, lane, st_t, st_d);
+  else
+    d = uniform_load(p.seq, b);
   if (d.mode != kDrawResidual) return;
   const int R = 2 * p.gamma + 1;
   const int jt = d.k, jd = p.gamma + 1 + d.k;
@@ -83,11 +92,15 @@ __global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p
   RawChunk<T, VW> rt, rd;
   load_raw<T, VW>(chain_row(tgt, drf, b, p.gamma, jt, p.V) + c * kChunk, nvalid, lane, rt);
   load_raw<T, VW>(chain_row(tgt, drf, b, p.gamma, jd, p.V) + c * kChunk, nvalid, lane, rd);
+  if (!decide_here) {
+    st_t = uniform_load(p.rowstat, b * R + jt);
+    st_d = uniform_load(p.rowstat, b * R + jd);
+  }
   const float te = effective_temperature(uniform_load(p.temp, b));
   const double w_c = residual_chunk_mass<T, VW>(
       rt, rd, nvalid, lane, uniform_load(p.part, (b * R + jt) * p.nchunk + c),
-      uniform_load(p.part, (b * R + jd) * p.nchunk + c), uniform_load(p.rowstat, b * R + jt),
-      uniform_load(p.rowstat, b * R + jd), double(te), log2e_over_t(te));
+      uniform_load(p.part, (b * R + jd) * p.nchunk + c), st_t, st_d, double(te),
+      log2e_over_t(te));
   if (lane == 0) p.wres[w] = w_c;
 }
 
@@ -307,6 +320,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   p.live_count = reinterpret_cast<int32_t*>(a.ws + L.off_live);
   p.live = p.live_count + kStageCountPad;
   p.hstat = reinterpret_cast<int32_t*>(a.ws + L.off_hstat);
+  p.reached = reinterpret_cast<int32_t*>(a.ws + L.off_reached);
   p.lz = reinterpret_cast<float*>(a.ws + L.off_lz);
 
   // The one-element-load forms of the one-workgroup kernel would spill; they take the split path.
@@ -330,16 +344,12 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
                           dim3(kStageDecideBlock), s, p, j);
         if (e != hipSuccess) return e;
       }
-      if (tail <= a.gamma) {
-        const hipError_t e = launch_kernel("chain_stage_rest", k_chain_stage_rest<T, VW>,
-                                           dim3(unsigned(a.B)), dim3(kStageRestBlock), s, p, tail);
-        if (e != hipSuccess) return e;
-      }
       const int64_t rtotal = int64_t(a.B) * L.nchunk;
       constexpr int rw = kResidualBlock / kWave;
       const hipError_t e = launch_kernel("chain_residual", k_chain_residual<T, VW>,
                                          dim3(unsigned(wave_groups(rtotal, rw))),
-                                         dim3(kResidualBlock), s, p, rtotal);
+                                         dim3(kResidualBlock), s, p, rtotal,
+                                         tail <= a.gamma ? tail : -1);
       if (e != hipSuccess) return e;
       return launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s,
                            p);
@@ -373,7 +383,8 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   const int64_t rtotal = int64_t(a.B) * L.nchunk;
   constexpr int rw = kResidualBlock / kWave;
   e = launch_kernel("chain_residual", k_chain_residual<T, VW>,
-                    dim3(unsigned(wave_groups(rtotal, rw))), dim3(kResidualBlock), s, p, rtotal);
+                    dim3(unsigned(wave_groups(rtotal, rw))), dim3(kResidualBlock), s, p, rtotal,
+                    -1);
   if (e != hipSuccess) return e;
   e = launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s, p);
   if (e != hipSuccess || !with_rates) return e;

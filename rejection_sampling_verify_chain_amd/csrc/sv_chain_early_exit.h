@@ -223,9 +223,10 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_lazy(ChainParams p) {
 // no logit row.  Few sequences are left after the first positions, and a launch that sweeps one
 // pair for them is mostly fixed cost, so from position kStageTailFrom on (when gamma >
 // kStageTailFrom) one sweep launch takes every remaining row of the sequences still in (pairs
-// kStageTailFrom .. gamma - 1 and the bonus row) and one more launch, chain_stage_rest, decides
-// those positions in order, one workgroup per sequence.  The
-// multi-kernel path's residual and draw kernels then finish every sequence from the decisions.
+// kStageTailFrom .. gamma - 1 and the bonus row).  The multi-kernel path's residual and draw
+// kernels then finish every sequence: the residual launch first tests those last positions in
+// order (finish_pending: every wave of such a sequence takes the decisions from the chunk
+// partials itself, and the chunk-0 wave writes them), then takes the residual masses of the cut.
 // Rows after the cut are read only by that last sweep and never change a result, and each step
 // calls the eager path's device functions on the same values, so the outputs agree with
 // sv_verify_chain bit for bit (p and q after the cut excepted).
@@ -257,24 +258,30 @@ inline int stage_groups(int j, int gamma, int64_t nchunk, int units_per_group) {
 // Decision of position i of sequence b (i == gamma: the bonus row) from the merged statistics of
 // target row i (a) and draft row i (d), with the drafted token's logits fetched earlier into lz
 // (one wave; the eager path's arithmetic).  lead: write the outputs, and at a cut or the bonus row
-// the decision and row statistics.  Returns whether the sequence goes on to position i + 1.
+// the decision and row statistics.  Returns whether the sequence goes on to position i + 1; when
+// it does not, *stop (if given) receives the decision.
 __device__ bool stage_decide(const ChainParams& p, int64_t b, int i, const RowStat& a,
-                             const RowStat& d, int status, double Td, bool lead, int lane) {
+                             const RowStat& d, int status, double Td, bool lead, int lane,
+                             SeqDecision* stop = nullptr) {
   const int gamma = p.gamma;
   const int R = 2 * gamma + 1;
   if (!a.valid || !d.valid) status |= SV_ROW_NONFINITE;
   if (status != 0) {
+    const SeqDecision dec{0, kDrawNone, status, 0};
     if (lead) {
       write_fallback(p, b, status, lane);
-      if (lane == 0) p.seq[b] = SeqDecision{0, kDrawNone, status, 0};
+      if (lane == 0) p.seq[b] = dec;
     }
+    if (stop) *stop = dec;
     return false;
   }
   if (i == gamma) {
+    const SeqDecision dec{gamma, kDrawBonus, 0, 0};
     if (lead && lane == 0) {
       p.rowstat[b * R + gamma] = a;
-      p.seq[b] = SeqDecision{gamma, kDrawBonus, 0, 0};
+      p.seq[b] = dec;
     }
+    if (stop) *stop = dec;
     return false;
   }
   const int x = uniform_load(p.toks, b * gamma + i);
@@ -305,7 +312,30 @@ __device__ bool stage_decide(const ChainParams& p, int64_t b, int i, const RowSt
       }
     }
   }
+  if (!accept && stop) *stop = SeqDecision{i, kDrawResidual, 0, 0};
   return accept;
+}
+
+// Positions s .. gamma of sequence b, which reached position s in the staged early exit's last
+// sweep (every remaining row swept, none tested yet), tested in order from the chunk partials (one
+// wave; each step as the decision launches take it).  lead: write the outputs, decision and row
+// statistics.  Returns the decision; at a cut, at and ad receive the cut pair's statistics.
+__device__ SeqDecision finish_pending(const ChainParams& p, int64_t b, int s, bool lead, int lane,
+                                      RowStat& at, RowStat& ad) {
+  const int gamma = p.gamma;
+  const int R = 2 * gamma + 1;
+  const double Td = effective_temperature(uniform_load(p.temp, b));
+  for (int i = s;; ++i) {  // wave-uniform; stage_decide stops at i == gamma at the latest
+    const RowStat a = merge_row(p.part + (b * R + i) * p.nchunk, p.nchunk, lane, Td);
+    const RowStat d =
+        i < gamma ? merge_row(p.part + (b * R + gamma + 1 + i) * p.nchunk, p.nchunk, lane, Td) : a;
+    SeqDecision stop;
+    if (!stage_decide(p, b, i, a, d, 0, Td, lead, lane, &stop)) {
+      at = a;
+      ad = d;
+      return stop;
+    }
+  }
 }
 
 // The drafted tokens' two logits at positions i = i0 + lane, i0 + lane + 64, ... < i1 (one wave),
@@ -370,7 +400,10 @@ k_chain_stage(ChainParams p, int j, int G) {
         bad |= (x < 0) || (int64_t(x) >= p.V);
       }
       if (__any(bad)) status |= SV_ROW_TOKEN_RANGE;
-      if (lane == 0) p.hstat[b] = status;
+      if (lane == 0) {
+        p.hstat[b] = status;
+        p.reached[b] = 0;
+      }
     }
     if (blockIdx.x == 0 && threadIdx.x == 0)  // the lists start empty each call
       for (int t = 0; t < kStageLists; ++t) p.live_count[t] = 0;
@@ -475,46 +508,14 @@ __global__ __launch_bounds__(kStageDecideBlock) void k_chain_stage_decide(ChainP
   const RowStat a = st2[0];
   const RowStat d = i < gamma ? st2[1] : a;
   const int status = i == 0 ? uniform_load(p.hstat, b) : 0;
-  if (stage_decide(p, b, i, a, d, status, Td, true, lane) && lane == 0 && i < kStageLists) {
+  if (stage_decide(p, b, i, a, d, status, Td, true, lane) && lane == 0) {
     // Reached position i + 1: list i.
-    const int32_t at = __hip_atomic_fetch_add(&p.live_count[i], 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    p.live[i * p.B + at] = int32_t(b);
-  }
-}
-
-// Positions s .. gamma - 1 and the bonus row of the sequences that reached position s, in order,
-// after launch s swept all their remaining rows (one 1024-thread workgroup per sequence): the
-// rows' partials are merged, a wave per row, then one wave takes the decisions.  Measured on 256
-// sequences of gamma = 7, V = 152064 fp32: 5.5 us against 6.7-6.9 us with 256 threads (the nine
-// merges of gamma - 3 pairs and the bonus row in one round of waves instead of three).
-constexpr int kStageRestBlock = 1024;
-template <typename T, int VW>
-__global__ __launch_bounds__(kStageRestBlock) void k_chain_stage_rest(ChainParams p, int s) {
-  __shared__ RowStat st[2 * kMaxGamma + 1];
-  // The rank-th sequence that reached position s (listed by launch s); the rest of the grid exits.
-  const int64_t rank = blockIdx.x;
-  const int32_t listed = uniform_load(p.live, (s - 1) * p.B + rank);  // rank < B: in the list
-  if (rank >= uniform_load(p.live_count, s - 1)) return;  // the whole workgroup
-  const int64_t b = listed;
-  const int gamma = p.gamma;
-  const int R = 2 * gamma + 1;
-  const int npos = gamma - s;
-  const int wave = wave_id();
-  const int lane = threadIdx.x & (kWave - 1);
-  const double Td = effective_temperature(uniform_load(p.temp, b));
-  // Merged row q: target row s + q (q < npos), draft row s + q - npos (q < 2 npos), the bonus row.
-  for (int q = wave; q < 2 * npos + 1; q += kStageRestBlock / kWave) {
-    const int row = q < npos ? s + q : q < 2 * npos ? gamma + 1 + s + (q - npos) : gamma;
-    const RowStat rs = merge_row(p.part + (b * R + row) * p.nchunk, p.nchunk, lane, Td);
-    if (lane == 0) st[q] = rs;
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  for (int i = s; i <= gamma; ++i) {  // wave-uniform
-    const RowStat a = i < gamma ? st[i - s] : st[2 * npos];
-    const RowStat d = i < gamma ? st[npos + i - s] : a;
-    if (!stage_decide(p, b, i, a, d, 0, Td, true, lane)) break;
+    p.reached[b] = i + 1;
+    if (i < kStageLists) {
+      const int32_t at = __hip_atomic_fetch_add(&p.live_count[i], 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      p.live[i * p.B + at] = int32_t(b);
+    }
   }
 }
 

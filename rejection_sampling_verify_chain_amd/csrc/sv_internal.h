@@ -99,12 +99,13 @@ constexpr int kStageLists = 3;
 constexpr int kStageCountPad = 64;  // int32 slots before the lists
 
 // Workspace: per (row, chunk) partials, per row statistics, per sequence decisions, per
-// (sequence, chunk) residual masses, and the staged early exit's sequence lists, input checks and
-// drafted logits.  Every entry is written before it is read within a call.
+// (sequence, chunk) residual masses, and the staged early exit's sequence lists, input checks,
+// last positions reached and drafted logits.  Every entry is written before it is read within a call.
 // with_rates: also the per (sequence, position, chunk) overlap sums of the acceptance rates.
 struct ChainLayout {
   int64_t nchunk;
-  size_t off_part, off_rowstat, off_seq, off_wres, off_live, off_hstat, off_lz, off_alpha_sum,
+  size_t off_part, off_rowstat, off_seq, off_wres, off_live, off_hstat, off_reached, off_lz,
+      off_alpha_sum,
       total;
 };
 
@@ -124,6 +125,8 @@ inline ChainLayout chain_layout(int64_t B, int64_t gamma, int64_t V, bool with_r
   L.off_live = off;  // staged early exit: counts [kStageCountPad], lists [kStageLists][B] int32
   off += align256(sizeof(int32_t) * (kStageCountPad + size_t(kStageLists) * size_t(B)));
   L.off_hstat = off;  // [B] int32
+  off += align256(sizeof(int32_t) * size_t(B));
+  L.off_reached = off;  // [B] int32
   off += align256(sizeof(int32_t) * size_t(B));
   L.off_lz = off;  // [B][gamma][2] fp32
   off += align256(sizeof(float) * 2 * size_t(B) * size_t(gamma));

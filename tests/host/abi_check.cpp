@@ -107,6 +107,7 @@ hipError_t launch_chain(const ChainArgs& a, hipStream_t) {
              {L.off_wres, size_t(mul(mul(a.B, L.nchunk), sizeof(double)))},
              {L.off_live, size_t(mul(mul(a.B, kStageLists) + kStageCountPad, sizeof(int32_t)))},
              {L.off_hstat, size_t(mul(a.B, sizeof(int32_t)))},
+             {L.off_reached, size_t(mul(a.B, sizeof(int32_t)))},
              {L.off_lz, size_t(mul(mul(a.B, a.gamma), 2 * sizeof(float)))},
              {L.off_alpha_sum,
               rates ? size_t(mul(mul(mul(a.B, a.gamma), L.nchunk), sizeof(double))) : 0}},
