@@ -65,10 +65,11 @@ __global__ __launch_bounds__(kBlock) void k_chain_decide(ChainParams p) {
 // The wave's chunk loads of both rows are issued as soon as the decision (which row) is known;
 // the chunk partials and row statistics that scale them arrive through the scalar cache while
 // the chunk is in flight.  A chunk whose target part is all -inf (A = 0) is loaded too and adds
-// nothing.  pending (staged early exit, else -1): a sequence that reached this position in the
-// last sweep has no decision yet; each of its waves takes the decisions from the chunk partials
-// itself (finish_pending; the chunk-0 wave writes them), with the cut pair's statistics in hand.
-template <typename T, int VW>
+// nothing.  PENDING (the staged early exit's form): a sequence that reached position `pending` in
+// the last sweep has no decision yet; each of its waves takes the decisions from the chunk
+// partials itself (finish_pending; the chunk-0 wave writes them), with the cut pair's statistics
+// in hand.  The other forms keep the plain kernel (one fewer dependent load ahead of the rows).
+template <typename T, int VW, bool PENDING>
 __global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p, int64_t total,
                                                                    int pending) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kResidualBlock) void k_chain_residual(ChainParams p
   if (w >= total) return;  // wave-uniform
   const int64_t b = w / p.nchunk;
   const int64_t c = w - b * p.nchunk;
-  const bool decide_here = pending >= 0 && uniform_load(p.reached, b) == pending;
+  const bool decide_here = PENDING && uniform_load(p.reached, b) == pending;
   RowStat st_t{}, st_d{};
   SeqDecision d;
   if (decide_here)
@@ -346,10 +347,12 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
       }
       const int64_t rtotal = int64_t(a.B) * L.nchunk;
       constexpr int rw = kResidualBlock / kWave;
-      const hipError_t e = launch_kernel("chain_residual", k_chain_residual<T, VW>,
-                                         dim3(unsigned(wave_groups(rtotal, rw))),
-                                         dim3(kResidualBlock), s, p, rtotal,
-                                         tail <= a.gamma ? tail : -1);
+      const dim3 rgrid(unsigned(wave_groups(rtotal, rw)));
+      const hipError_t e =
+          tail <= a.gamma ? launch_kernel("chain_residual", k_chain_residual<T, VW, true>, rgrid,
+                                          dim3(kResidualBlock), s, p, rtotal, tail)
+                          : launch_kernel("chain_residual", k_chain_residual<T, VW, false>, rgrid,
+                                          dim3(kResidualBlock), s, p, rtotal, -1);
       if (e != hipSuccess) return e;
       return launch_kernel("chain_draw", k_chain_draw<T, VW>, dim3(unsigned(a.B)), dim3(kWave), s,
                            p);
@@ -382,7 +385,7 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int64_t rtotal = int64_t(a.B) * L.nchunk;
   constexpr int rw = kResidualBlock / kWave;
-  e = launch_kernel("chain_residual", k_chain_residual<T, VW>,
+  e = launch_kernel("chain_residual", k_chain_residual<T, VW, false>,
                     dim3(unsigned(wave_groups(rtotal, rw))), dim3(kResidualBlock), s, p, rtotal,
                     -1);
   if (e != hipSuccess) return e;

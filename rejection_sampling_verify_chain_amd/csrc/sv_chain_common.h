@@ -566,39 +566,11 @@ __device__ __forceinline__ double residual_chunk_mass(const RawChunk<T, VW>& rt,
                                                       const RowPart& pd, const RowStat& st_t,
                                                       const RowStat& st_d, double Td, float kk) {
   const ResidualScale rs = residual_scale(chunk_scale(pt.m, st_t, Td), chunk_scale(pd.m, st_d, Td));
-  double lsum;
-  if constexpr (VW == 1) {
-    float zt[kElemsPerLane], zd[kElemsPerLane];
-    unpack_chunk<T, VW>(rt, nvalid, lane, zt);
-    unpack_chunk<T, VW>(rd, nvalid, lane, zd);
-    lsum = lane_term_sum([&](int i) { return residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs); });
-  } else {
-    // lane_term_sum's order (groups of four in fp32, two alternating fp64 accumulators), taken
-    // one load at a time from the raw vectors with unpack_chunk's masking of loads past the
-    // row, so that the two widened chunks are never held whole.
-    static_assert(VW % 4 == 0, "a load holds whole groups of four");
-    double acc[2] = {0.0, 0.0};
-#pragma unroll
-    for (int j = 0; j < kElemsPerLane / VW; ++j) {
-      float zt[VW], zd[VW];
-      unpack<T, VW>(rt.v[j], zt);
-      unpack<T, VW>(rd.v[j], zd);
-      if (nvalid != kChunk && !((j * kWave + lane) * VW < nvalid)) {
-#pragma unroll
-        for (int t = 0; t < VW; ++t) zt[t] = zd[t] = -INFINITY;
-      }
-#pragma unroll
-      for (int g = 0; g < VW; g += 4) {
-        const float t = (residual_term(zt[g], zd[g], pt.m, pd.m, kk, rs) +
-                         residual_term(zt[g + 1], zd[g + 1], pt.m, pd.m, kk, rs)) +
-                        (residual_term(zt[g + 2], zd[g + 2], pt.m, pd.m, kk, rs) +
-                         residual_term(zt[g + 3], zd[g + 3], pt.m, pd.m, kk, rs));
-        acc[((j * VW + g) >> 2) & 1] += double(t);
-      }
-    }
-    lsum = acc[0] + acc[1];
-  }
-  const double wsum = wave_sum(lsum);
+  float zt[kElemsPerLane], zd[kElemsPerLane];
+  unpack_chunk<T, VW>(rt, nvalid, lane, zt);
+  unpack_chunk<T, VW>(rd, nvalid, lane, zd);
+  const double wsum = wave_sum(lane_term_sum(
+      [&](int i) { return residual_term(zt[i], zd[i], pt.m, pd.m, kk, rs); }));
   return rs.A > 0.0 ? rs.A * wsum : 0.0;
 }
 
