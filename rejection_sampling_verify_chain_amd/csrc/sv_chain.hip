@@ -245,9 +245,10 @@ constexpr int kFinishMaxBatch = 512;
 // two forms, one launch per position (staged) pays for wide rows, whose pair of rows one CU would
 // read slowly, and one workgroup per sequence for narrow ones, where the launches' fixed cost
 // would dominate.  Measured per call (staged / one workgroup / eager): B = 256, gamma = 7,
-// V = 152064 fp32: 190 / 225 / 400 us; B = 128, same rows: 134 / 208 / 213 us; B = 1024,
-// gamma = 4, V = 32000 bf16: 115 / 118 / 151 us; B = 512, gamma = 7, V = 32000 bf16 with drafts
-// close to the target: 125 / 111 / 122 us; B = 64, gamma = 4, V = 128256 bf16: 66 / 102 / 48 us.
+// V = 152064 fp32: 171 / 223 / 398 us; B = 128, same rows: 113 / 195 / 211 us; B = 256,
+// gamma = 7, V = 131072 bf16: 141 / 164 / 209 us; B = 256, gamma = 7, V = 65536 bf16: 105 / 93 /
+// 114 us; B = 512, gamma = 4, V = 65536 bf16: 123 / 125 / 151 us; B = 1024, gamma = 4,
+// V = 32000 bf16: 134 / 132 / 151 us; B = 64, gamma = 4, V = 128256 bf16: 63 / 102 / 47 us.
 // SPECVERIFY_CHAIN_PATH=lazy or staged forces a form (testing).
 constexpr int kLazyMinBatch = 128;
 constexpr int64_t kStagedMinPairBytes = 256 * 1024;

@@ -233,24 +233,26 @@ __global__ __launch_bounds__(kFusedBlock) void k_chain_lazy(ChainParams p) {
 
 constexpr int kStageBlock = 256;
 constexpr int kStageWavesPerSimd = 8;
-// First position whose launch sweeps all the remaining rows (see above); that launch keeps two
-// chunks per wave in flight, at the occupancy their registers allow.
-// Measured on 256 sequences of gamma = 7, V = 152064 fp32 (mean accepted 0.56) per call: one
-// launch per position 187.6-188.0 us; all remaining rows from position 3 on 182.3-183.3 us, from
-// position 2 on 191.9-192.6 us, from position 4 on 185.2-185.4 us.
+// First position whose sweep takes all the remaining rows (see above); that launch keeps two
+// chunks per wave in flight, at the occupancy their registers allow.  Measured on 256 sequences
+// of gamma = 7, V = 152064 fp32 (mean accepted 0.56) per call, with the decisions in their own
+// launches: all remaining rows from position 3 on 173.8-174.7 us, from position 4 on 178.9 us,
+// from position 5 on 183.3 us (and, with the decisions inside the sweeps, one launch per
+// position 187.6-188.0 us, from position 2 on 191.9-192.6 us).
 constexpr int kStageTailFrom = 3;
 constexpr int kStageTailWavesPerSimd = 4;
 static_assert(kStageTailFrom <= kStageLists,
-              "launches 2 .. kStageTailFrom and the last step each read a list of the workspace");
+              "the sweeps and decisions of positions 1 .. kStageTailFrom read lists "
+              "0 .. kStageTailFrom - 1 of the workspace");
 
-// The launch that sweeps all remaining rows, or gamma + 2 (none) for short drafts.
+// The position whose sweep takes all the remaining rows, or gamma + 2 (none) for short drafts.
 inline int stage_tail(int gamma) { return gamma > kStageTailFrom ? kStageTailFrom : gamma + 2; }
 template <typename T>
 constexpr int kStageUnits = (kStageBlock / kWave) * kUnitsPerWave<T>;  // chunks per workgroup
 
-// Workgroups per sequence in launch j: enough for the largest slice work of that launch.
+// Workgroups per sequence in the sweep of position j <= gamma: one slice of row pair j each (of
+// target row gamma alone at j = gamma); the sweep of all remaining rows strides over them.
 inline int stage_groups(int j, int gamma, int64_t nchunk, int units_per_group) {
-  if (j > gamma) return 1;
   const int64_t units = (j < gamma ? 2 : 1) * nchunk;
   return int((units + units_per_group - 1) / units_per_group);
 }
