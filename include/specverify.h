@@ -161,11 +161,14 @@ sv_status sv_verify_chain_noalloc(const void* target_logits, const void* draft_l
  * out_p / out_q at positions i <= k; after the cut they are NaN where the row was not read and
  * sv_verify_chain's values elsewhere.
  * Rows after the cut may not be read: a non-finite value there may or may not set
- * SV_ROW_NONFINITE and the fallback.  Batches of at least 128 sequences take the positions in
- * order, reading target and draft row i only once position i is reached (and target row gamma
- * only if every draft is accepted): with rows of 128 KiB or more, one launch per position across
- * the whole chip (gamma + 2 launches, then the residual and draw kernels); with narrower rows,
- * one launch with one workgroup per sequence.  Smaller batches run as sv_verify_chain.
+ * SV_ROW_NONFINITE and the fallback.  Batches with enough rows take the positions in order,
+ * reading target and draft row i only once position i is reached (and target row gamma only if
+ * every draft is accepted): for wide rows (a target and draft row of 512 KiB or more together,
+ * or 256 KiB from 384 sequences on, or a first row pair of 48 MiB or more over the batch below
+ * 256 sequences) two launches per position across the whole chip, the last of them taking
+ * every remaining row, then the residual and draw kernels; from 256 sequences on with narrower
+ * rows, one launch with one workgroup per sequence.  Other batches (and every batch below 128
+ * sequences) run as sv_verify_chain.
  * SPECVERIFY_CHAIN_PATH=staged or =lazy, read on every call, forces the one-launch-per-position
  * form or the one-workgroup form at any batch size (testing and measurement; the one-workgroup
  * form needs the row pair's partials to fit 32 KiB of LDS).

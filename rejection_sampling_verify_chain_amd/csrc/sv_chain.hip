@@ -240,18 +240,29 @@ constexpr int kChipFillMin = 192, kChipFillMax = 256;  // fused whatever the row
 constexpr int64_t kFinishMaxResidualBytes = 256 * 1024;
 constexpr int kFinishMaxBatch = 512;
 
-// Early exit (sv_verify_chain_lazy) pays once the sequences give most CUs work; smaller batches
-// take the eager paths, whose outputs agree wherever the early-exit contract fixes them.  Of the
-// two forms, one launch per position (staged) pays for wide rows, whose pair of rows one CU would
-// read slowly, and one workgroup per sequence for narrow ones, where the launches' fixed cost
-// would dominate.  Measured per call (staged / one workgroup / eager): B = 256, gamma = 7,
+// Early exit (sv_verify_chain_lazy) pays once the batch holds enough rows; smaller batches take
+// the eager paths, whose outputs agree wherever the early-exit contract fixes them.  One
+// workgroup per sequence pays once every CU has a sequence and the row pairs are narrow (a CU
+// reads its sequence's pairs one after another); one launch per position (staged) pays for wide
+// pairs, and for narrower ones in large batches.  The gate (lazy_form), with W = B x (bytes of
+// one row pair): below kLazyMinBatch sequences eager; pairs of kStagedWidePairBytes or more
+// staged; below kLazyGroupBatch sequences staged when W >= kStagedMinFirstPairs, else eager;
+// otherwise staged for pairs of kStagedMinPairBytes or more from kStagedBatch sequences on, else
+// one workgroup per sequence.  Measured per call (staged / one workgroup / eager): B = 256, gamma = 7,
 // V = 152064 fp32: 171 / 223 / 398 us; B = 128, same rows: 113 / 195 / 211 us; B = 256,
 // gamma = 7, V = 131072 bf16: 141 / 164 / 209 us; B = 256, gamma = 7, V = 65536 bf16: 105 / 93 /
 // 114 us; B = 512, gamma = 4, V = 65536 bf16: 123 / 125 / 151 us; B = 1024, gamma = 4,
-// V = 32000 bf16: 134 / 132 / 151 us; B = 64, gamma = 4, V = 128256 bf16: 63 / 102 / 47 us.
+// V = 32000 bf16: 134 / 132 / 151 us; B = 64, gamma = 4, V = 128256 bf16: 63 / 102 / 47 us;
+// B = 128, gamma = 7, V = 65536 bf16: 75 / 88 / 64 us; B = 128, gamma = 7, V = 98304 bf16:
+// 85 / 125 / 91 us; B = 192, gamma = 7, V = 65536 bf16: 84 / 90 / 100 us; B = 384, gamma = 7,
+// V = 65536 bf16: 122 / 132 / 168 us; B = 128, gamma = 7, V = 32000 bf16: 62 / 54 / 39 us.
 // SPECVERIFY_CHAIN_PATH=lazy or staged forces a form (testing).
 constexpr int kLazyMinBatch = 128;
-constexpr int64_t kStagedMinPairBytes = 256 * 1024;
+constexpr int kLazyGroupBatch = 256;                        // one workgroup per sequence from here
+constexpr int kStagedBatch = 384;                           // staged for mid-width pairs from here
+constexpr int64_t kStagedMinPairBytes = 256 * 1024;         // mid-width pairs
+constexpr int64_t kStagedWidePairBytes = 512 * 1024;        // wide pairs: staged at any batch
+constexpr int64_t kStagedMinFirstPairs = int64_t(48) << 20;  // W below kLazyGroupBatch
 
 inline size_t lazy_lds_bytes(int64_t nchunk) {
   return (2 * sizeof(RowPart) + sizeof(double)) * size_t(nchunk);
@@ -271,8 +282,12 @@ inline LazyForm lazy_form(const ChainArgs& a, int64_t nchunk, int units_per_grou
   if (e && (strcmp(e, "fused") == 0 || strcmp(e, "finish") == 0 || strcmp(e, "split") == 0))
     return LazyForm::kNone;
   if (a.B < kLazyMinBatch) return LazyForm::kNone;
-  if (2 * a.V * int64_t(elem_bytes) >= kStagedMinPairBytes || !group_ok)
-    return staged_ok ? LazyForm::kStaged : LazyForm::kNone;
+  const int64_t pair = 2 * a.V * int64_t(elem_bytes);
+  const LazyForm staged = staged_ok ? LazyForm::kStaged : LazyForm::kNone;
+  if (pair >= kStagedWidePairBytes) return staged;
+  if (a.B < kLazyGroupBatch)
+    return int64_t(a.B) * pair >= kStagedMinFirstPairs ? staged : LazyForm::kNone;
+  if ((pair >= kStagedMinPairBytes && a.B >= kStagedBatch) || !group_ok) return staged;
   return LazyForm::kOneGroup;
 }
 

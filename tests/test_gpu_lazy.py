@@ -164,8 +164,9 @@ def test_small_batch_runs_as_verify_chain():
 
 
 def test_batch_threshold_takes_early_exit():
-    b = I.chain_gaussian(15, 128, 4, 4096, "bf16", 2.0, 1.0, 1.0)
-    out = check_both(b, "B=128 auto")
+    # From 256 sequences on, narrow rows take the one-workgroup form: p, q NaN after the cut.
+    b = I.chain_gaussian(15, 256, 4, 4096, "bf16", 2.0, 1.0, 1.0)
+    out = check_both(b, "B=256 auto")
     k = out["num_accepted"]
     after = np.arange(4)[None, :] > k[:, None]
     assert after.any() and np.all(np.isnan(out["p"][after])) and np.all(np.isnan(out["q"][after]))

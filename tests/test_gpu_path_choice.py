@@ -61,9 +61,14 @@ def test_unaligned_rows_take_split(monkeypatch):
 
 @pytest.mark.parametrize("B,gamma,V,dtype,want", [
     (64, 3, 8000, "bf16", {"chain_fused"}),                       # below 128 sequences: eager
-    (128, 3, 8000, "bf16", {"chain_lazy"}),                       # narrow row pairs: one workgroup
-    (128, 3, 40000, "f32", {"chain_stage", "chain_stage_decide", "chain_residual",
-                            "chain_draw"}),                       # wide: staged
+    (128, 3, 8000, "bf16", {"chain_fused"}),                      # few rows: eager
+    (256, 3, 8000, "bf16", {"chain_lazy"}),                       # narrow row pairs: one workgroup
+    (128, 3, 70000, "f32", {"chain_stage", "chain_stage_decide", "chain_residual",
+                            "chain_draw"}),                       # wide pairs: staged
+    (192, 3, 65536, "bf16", {"chain_stage", "chain_stage_decide", "chain_residual",
+                             "chain_draw"}),                      # 48 MiB of first pairs: staged
+    (128, 3, 40000, "f32", {"chain_sweep", "chain_decide", "chain_residual",
+                            "chain_draw"}),                       # below that: eager (split)
 ])
 def test_early_exit_form_choice(B, gamma, V, dtype, want, monkeypatch):
     b = I.chain_gaussian(62 + B, B, gamma, V, dtype, 2.0, 1.0, 1.0)
