@@ -37,6 +37,26 @@ ALPHA_RTOL = 1e-5
 ALPHA_ATOL = 1e-12
 
 
+# Band rows allowed per full-size workload: twice the count its seeded inputs give (the accept
+# band and the edge band together, as tests/record_parity.py records them), so that a change
+# that widened the bands, or moved many rows into them, fails the parity tests.  At most a
+# quarter of that many (and at least 2) band rows may be resolved differently from the oracle.
+BAND_LIMITS = {
+    "zipf_b64_g4_v128256_bf16": 8,      # recorded: 4 edge-band rows of 64
+    "gauss_b256_g7_v152064_f32": 16,    # recorded: 8 edge-band rows of 256
+    "sample_b256_v152064_f32": 48,      # recorded: 24 of 256 rows
+    "sample_b64_v128256_bf16": 12,      # recorded: 6 of 64 rows
+}
+
+
+def assert_band_limit(name, counts):
+    """The band counts of a full-size workload stay within BAND_LIMITS."""
+    limit = BAND_LIMITS[name]
+    bands = counts.get("accept_band", 0) + counts["edge_band"]
+    assert bands <= limit, f"{name}: {bands} band rows, more than {limit}: {counts}"
+    assert counts["band_differs"] <= max(2, limit // 4), f"{name}: {counts}"
+
+
 def allowed_outcomes(target, draft, toks, uni, temp, res):
     """(k, tokens) pairs the GPU may return for this sequence, with a flag kind."""
     kind = "exact"

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity import check_chain
+from parity import BAND_LIMITS, assert_band_limit, check_chain
 from rejection_sampling_verify_chain_amd import binding as BD
 from rejection_sampling_verify_chain_amd import inputs as I
 
@@ -57,7 +57,10 @@ def check_both(batch, name, seqs=None, refs=None):
     """Early exit against the oracle and against the eager entry point on the same buffers."""
     d = BD.chain_to_device(batch)
     lazy = run(batch, True, d)
-    report(name, check_chain(batch, lazy, seqs, lazy=True, refs=refs))
+    counts = check_chain(batch, lazy, seqs, lazy=True, refs=refs)
+    report(name, counts)
+    if seqs is None and batch.name in BAND_LIMITS:
+        assert_band_limit(batch.name, counts)
     assert_same_as_eager(lazy, run(batch, False, d))
     return lazy
 

@@ -6,7 +6,7 @@ import torch
 from scipy import stats
 from scipy.special import softmax as sp_softmax
 
-from parity import check_sample
+from parity import assert_band_limit, check_sample
 from rejection_sampling_verify_chain_amd import binding as BD
 from rejection_sampling_verify_chain_amd import inputs as I
 
@@ -31,6 +31,7 @@ def test_full_size_workloads(name):
     b = I.SAMPLE_WORKLOADS[name]()
     c = check_sample(b, run_sample(b))
     print(f"[parity] {name}: {c}", flush=True)
+    assert_band_limit(name, c)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
