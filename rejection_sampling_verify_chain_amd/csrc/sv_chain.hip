@@ -126,14 +126,23 @@ __global__ __launch_bounds__(kWave) void k_chain_draw(ChainParams p) {
 struct FusedShared {
   RowStat st[2 * kMaxGamma + 1];
   SeqDecision d;
+  int last;
 };
 
 // The body of chain_fused and chain_finish (all threads of the sequence's workgroup); fused_lds
-// is the launch's dynamic LDS: partials [R][nchunk], then residual masses [nchunk].
-template <typename T, int VW, bool SWEPT>
+// is the launch's dynamic LDS: partials [R][nchunk], then residual masses [nchunk].  With G > 1
+// (chain_finish on small batches) G workgroups share each sequence: every one copies and merges
+// its partials and takes the decision; the first writes the results; each computes the residual
+// masses of every G-th chunk and publishes them (publish_mass), and the last to arrive draws.
+// That spreads the residual pass, bound by its two exponentials per element on one compute
+// unit, over G of them.
+template <typename T, int VW, bool SWEPT, int G>
 __device__ __forceinline__ void one_workgroup_chain(const ChainParams& p, unsigned char* fused_lds,
                                                     FusedShared& sh) {
-  const int64_t b = blockIdx.x;
+  static_assert(G == 1 || SWEPT, "several workgroups per sequence only after the sweep");
+  const int64_t b = G == 1 ? int64_t(blockIdx.x) : int64_t(blockIdx.x / G);
+  const int grp = G == 1 ? 0 : int(blockIdx.x % G);
+  const bool lead = grp == 0;
   const int gamma = p.gamma;
   const int R = 2 * gamma + 1;
   const int64_t V = p.V, nchunk = p.nchunk;
@@ -189,12 +198,12 @@ __device__ __forceinline__ void one_workgroup_chain(const ChainParams& p, unsign
     const RowStat st = merge_row(prt + int64_t(j) * nchunk, nchunk, lane, Td);
     if (lane == 0) {
       sh.st[j] = st;
-      if (SWEPT) p.rowstat[b * R + j] = st;
+      if (SWEPT && lead) p.rowstat[b * R + j] = st;
     }
   }
   __syncthreads();
   if (wave == 0) {
-    const SeqDecision d = decide_from_stats(p, b, sh.st, g, tb, Td, lane);
+    const SeqDecision d = decide_from_stats(p, b, sh.st, g, tb, Td, lane, lead);
     if (lane == 0) sh.d = d;
   }
   __syncthreads();
@@ -202,7 +211,7 @@ __device__ __forceinline__ void one_workgroup_chain(const ChainParams& p, unsign
   if (d.mode == kDrawNone) return;  // the whole workgroup: the decision wrote the result
   if (d.mode == kDrawResidual) {     // the whole workgroup
     const int jt = d.k, jd = gamma + 1 + d.k;
-    for (int64_t c = wave; c < nchunk; c += kFusedWaves) {
+    for (int64_t c = grp + int64_t(G) * wave; c < nchunk; c += int64_t(G) * kFusedWaves) {
       const int nvalid = chunk_valid(V, c);
       RawChunk<T, VW> rt, rd;
       load_raw<T, VW>(chain_row(tgt, drf, b, gamma, jt, V) + c * kChunk, nvalid, lane, rt);
@@ -210,26 +219,43 @@ __device__ __forceinline__ void one_workgroup_chain(const ChainParams& p, unsign
       const double w_c = residual_chunk_mass<T, VW>(rt, rd, nvalid, lane, prt[jt * nchunk + c],
                                                     prt[jd * nchunk + c], sh.st[jt], sh.st[jd],
                                                     Td, kk);
-      if (lane == 0) wr[c] = w_c;
+      if (lane == 0) {
+        if constexpr (G == 1)
+          wr[c] = w_c;
+        else
+          publish_mass(p.wres + b * nchunk + c, w_c);
+      }
     }
     __syncthreads();
+    if constexpr (G > 1) {
+      if (threadIdx.x == 0)
+        sh.last = __hip_atomic_fetch_add(p.arrive + b, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == G - 1;
+      __syncthreads();
+      if (!sh.last) return;  // the whole workgroup
+    }
+  } else if (!lead) {
+    return;  // the bonus draw is the first workgroup's
   }
   if (wave != 0) return;
-  draw_sequence<T, VW>(p, b, d, LdsSrc{sh.st, prt, wr, nchunk});
+  if constexpr (G == 1)
+    draw_sequence<T, VW>(p, b, d, LdsSrc{sh.st, prt, wr, nchunk});
+  else
+    draw_sequence<T, VW>(p, b, d, LdsPublishedSrc{sh.st, prt, p.wres + b * nchunk, nchunk});
 }
 
 template <typename T, int VW>
 __global__ __launch_bounds__(kFusedBlock) void k_chain_fused(ChainParams p) {
   extern __shared__ __align__(16) unsigned char fused_lds[];
   __shared__ FusedShared sh;
-  one_workgroup_chain<T, VW, false>(p, fused_lds, sh);
+  one_workgroup_chain<T, VW, false, 1>(p, fused_lds, sh);
 }
 
-template <typename T, int VW>
+template <typename T, int VW, int G>
 __global__ __launch_bounds__(kFusedBlock) void k_chain_finish(ChainParams p) {
   extern __shared__ __align__(16) unsigned char fused_lds[];
   __shared__ FusedShared sh;
-  one_workgroup_chain<T, VW, true>(p, fused_lds, sh);
+  one_workgroup_chain<T, VW, true, G>(p, fused_lds, sh);
 }
 
 enum class ChainPath { kSplit, kFused, kFinish };
@@ -239,6 +265,19 @@ constexpr int64_t kFusedMaxSeqBytes = 256 * 1024;    // small rows: fused for B 
 constexpr int kChipFillMin = 192, kChipFillMax = 256;  // fused whatever the row size
 constexpr int64_t kFinishMaxResidualBytes = 256 * 1024;
 constexpr int kFinishMaxBatch = 512;
+// Workgroups per sequence in chain_finish: for rows of 16 chunks or more, 4 up to 64 sequences
+// and 2 up to 128 (the launch stays within one 1024-thread workgroup per compute unit), else 1.
+// With fewer chunks one workgroup's residual pass has at most two chunk pairs per SIMD, and the
+// hand-off costs what the split saves.  Measured per call, one workgroup against the split:
+// B = 1, gamma = 4, V = 32000 bf16 16.0-16.4 against 13.4-14.1 us; B = 32 19.6 against 17.7 us;
+// B = 64 23.1-23.3 against 21.4 us; B = 64, V = 65536 bf16 33.8-33.9 against 28.6-28.8 us;
+// B = 96, V = 32000 bf16 26.2 against 25.2 us (2 per sequence); B = 128 29.5-29.6 against
+// 28.7-28.8 us; B = 128, V = 65536 bf16 46.3 against 43.9 us; 8-chunk fp32 rows (V = 16384,
+// gamma = 7): B = 64 24.9 against 24.9 us, B = 128 34.0 against 34.9 us.
+inline int finish_groups(int B, int64_t nchunk) {
+  if (nchunk < 16) return 1;
+  return B <= 64 ? 4 : B <= 128 ? 2 : 1;
+}
 
 // Early exit (sv_verify_chain_lazy) pays once the batch holds enough rows; smaller batches take
 // the eager paths, whose outputs agree wherever the early-exit contract fixes them.  One
@@ -381,6 +420,8 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
                                dim3(kFusedBlock), fused_lds_bytes(a.gamma, L.nchunk), s, p);
   }
 
+  const int fg = VW > 1 && path == ChainPath::kFinish ? finish_groups(a.B, L.nchunk) : 1;
+  if (fg > 1) p.arrive = p.reached;  // the staged early exit's record, unused here
   const int64_t total = int64_t(a.B) * (2 * a.gamma + 1) * L.nchunk;
   const int64_t waves = (total + kUnitsPerWave<T> - 1) / kUnitsPerWave<T>;
   constexpr int wpb = kStreamBlock<T> / kWave;
@@ -390,8 +431,14 @@ hipError_t run_chain(const ChainArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   if constexpr (VW > 1) {
     if (path == ChainPath::kFinish) {
-      e = launch_kernel_shm("chain_finish", k_chain_finish<T, VW>, dim3(unsigned(a.B)),
-                            dim3(kFusedBlock), fused_lds_bytes(a.gamma, L.nchunk), s, p);
+      const size_t lds = fused_lds_bytes(a.gamma, L.nchunk);
+      const dim3 grid(unsigned(a.B * fg));
+      e = fg == 4   ? launch_kernel_shm("chain_finish", k_chain_finish<T, VW, 4>, grid,
+                                        dim3(kFusedBlock), lds, s, p)
+          : fg == 2 ? launch_kernel_shm("chain_finish", k_chain_finish<T, VW, 2>, grid,
+                                        dim3(kFusedBlock), lds, s, p)
+                    : launch_kernel_shm("chain_finish", k_chain_finish<T, VW, 1>, grid,
+                                        dim3(kFusedBlock), lds, s, p);
       if (e != hipSuccess || !with_rates) return e;
       return launch_alpha_tail<T, VW>(p, a.B, reinterpret_cast<double*>(a.ws + L.off_alpha_sum),
                                       a.out_alpha, nullptr, s);

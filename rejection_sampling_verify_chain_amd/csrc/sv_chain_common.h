@@ -46,6 +46,8 @@ struct ChainParams {
   int32_t* hstat = nullptr;
   int32_t* reached = nullptr;
   float* lz = nullptr;
+  // chain_finish over several workgroups per sequence: arrival counts [B], zeroed by the sweep.
+  int32_t* arrive = nullptr;
 };
 
 template <typename T>
@@ -234,7 +236,8 @@ __device__ __forceinline__ Drafted gather_drafted(const ChainParams& p, int64_t 
 // Writes p, q, the accepted prefix with its padding, and the fallback result; returns the
 // decision (the same on every lane).
 __device__ SeqDecision decide_from_stats(const ChainParams& p, int64_t b, const RowStat* st,
-                                         const Drafted& g, float tb, double Td, int lane) {
+                                         const Drafted& g, float tb, double Td, int lane,
+                                         bool write = true) {
   const int gamma = p.gamma;
   const int R = 2 * gamma + 1;
   int status = 0;
@@ -266,25 +269,27 @@ __device__ SeqDecision decide_from_stats(const ChainParams& p, int64_t b, const 
       } else {
         accept = (pi > 0.0) && (u < 1.0);  // ratio +inf; p = q = 0 rejects
       }
-      if (p.out_p) p.out_p[b * gamma + lane] = float(pi);
-      if (p.out_q) p.out_q[b * gamma + lane] = float(qi);
+      if (write && p.out_p) p.out_p[b * gamma + lane] = float(pi);
+      if (write && p.out_q) p.out_q[b * gamma + lane] = float(qi);
     }
     // k = number of leading ones of the accept mask.
     const uint64_t rej = ~uint64_t(__ballot(accept && lane < gamma));
     const int lead = rej == 0 ? kWave : __builtin_ctzll(rej);
     k = lead < gamma ? lead : gamma;
-  } else if (lane < gamma) {
+  } else if (write && lane < gamma) {
     if (p.out_p) p.out_p[b * gamma + lane] = NAN;
     if (p.out_q) p.out_q[b * gamma + lane] = NAN;
   }
-  // Accepted prefix and padding; position k is written by the draw.
-  for (int i = lane; i <= gamma; i += kWave) {
+  // Accepted prefix and padding.  Position k is the draw's alone (chain_finish's several-workgroup
+  // form draws in another workgroup, whose store no store here may follow).
+  for (int i = lane; write && i <= gamma; i += kWave) {
+    if (i == k && !fallback) continue;
     int32_t v = -1;
     if (i < k) v = g.x;  // i < k <= gamma <= 64 only on the first pass, where lane i holds x_i
     if (fallback && i == 0) v = 0;
     p.out_tokens[b * (gamma + 1) + i] = v;
   }
-  if (fallback && lane == 0) {
+  if (write && fallback && lane == 0) {
     p.out_nacc[b] = 0;
     if (p.out_status) p.out_status[b] = status;
   }
@@ -448,6 +453,27 @@ struct WorkspaceSrc {
   __device__ double wres(int64_t c) const { return p.wres[b * p.nchunk + c]; }
 };
 
+// Hand-off between the workgroups of one sequence in chain_finish's several-workgroup form,
+// within one launch and without a fence.  A wave publishes a chunk mass with an agent-scope
+// atomic exchange and waits for it to return, so it has been performed where the atomics of
+// every XCD meet before the workgroup's arrival is counted (an agent-scope atomic add after a
+// workgroup barrier).  The workgroup whose arrival completes the count draws, reading the masses
+// back with agent-scope atomic read-modify-writes (fetch-or 0), which are performed after that
+// last arrival and so return every published value.  Every access to the masses and the counts
+// in the launch is atomic; the counts were zeroed by the sweep, the launch before.
+__device__ __forceinline__ void publish_mass(double* dst, double v) {
+  const uint64_t old = __hip_atomic_exchange(reinterpret_cast<uint64_t*>(dst),
+                                             __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("" ::"v"(old) : "memory");  // the returned value is waited on here
+}
+
+__device__ __forceinline__ double read_published(double* src) {
+  return __builtin_bit_cast(double,
+                            __hip_atomic_fetch_or(reinterpret_cast<uint64_t*>(src), uint64_t(0),
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 struct LdsSrc {
   const RowStat* st;   // [2 * gamma + 1]
   const RowPart* prt;  // [2 * gamma + 1][nchunk]
@@ -457,6 +483,18 @@ struct LdsSrc {
   __device__ RowPart part(int j, int64_t c) const { return prt[j * nchunk + c]; }
   __device__ RowPart part_lane(int j, int64_t c) const { return prt[j * nchunk + c]; }
   __device__ double wres(int64_t c) const { return wr[c]; }
+};
+
+// Row statistics and partials from LDS, residual masses published by the sequence's workgroups.
+struct LdsPublishedSrc {
+  const RowStat* st;   // [2 * gamma + 1]
+  const RowPart* prt;  // [2 * gamma + 1][nchunk]
+  double* wr;          // [nchunk], in the workspace
+  int64_t nchunk;
+  __device__ RowStat stat(int j) const { return st[j]; }
+  __device__ RowPart part(int j, int64_t c) const { return prt[j * nchunk + c]; }
+  __device__ RowPart part_lane(int j, int64_t c) const { return prt[j * nchunk + c]; }
+  __device__ double wres(int64_t c) const { return read_published(wr + c); }
 };
 
 // Draw of sequence b (one wave): residual draw over the residual chunk masses (falling back to
@@ -554,6 +592,7 @@ __global__ __launch_bounds__(kStreamBlock<T>, kStreamWavesPerSimd<VW>) void k_ch
         const RowPart rp =
             reduce_chunk(z, log2e_over_t(effective_temperature(uniform_load(p.temp, k.b))));
         if (lane == 0) p.part[k.w] = rp;
+        if (p.arrive != nullptr && k.j == 0 && k.c == 0 && lane == 0) p.arrive[k.b] = 0;
       });
 }
 
