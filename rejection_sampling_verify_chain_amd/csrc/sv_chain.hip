@@ -274,6 +274,7 @@ constexpr int kFinishMaxBatch = 512;
 // B = 96, V = 32000 bf16 26.2 against 25.2 us (2 per sequence); B = 128 29.5-29.6 against
 // 28.7-28.8 us; B = 128, V = 65536 bf16 46.3 against 43.9 us; 8-chunk fp32 rows (V = 16384,
 // gamma = 7): B = 64 24.9 against 24.9 us, B = 128 34.0 against 34.9 us.
+constexpr int kFinishGroupsMinBatch = 16;  // wide rows: chain_finish from here (choose_path)
 inline int finish_groups(int B, int64_t nchunk) {
   if (nchunk < 16) return 1;
   return B <= 64 ? 4 : B <= 128 ? 2 : 1;
@@ -346,6 +347,14 @@ inline ChainPath choose_path(const ChainArgs& a, int64_t nchunk, size_t elem_byt
   if (a.B <= kChipFillMax && int64_t(2 * a.gamma + 1) * a.V * s <= kFusedMaxSeqBytes) return fused;
   if (a.B >= kChipFillMin && a.B <= kChipFillMax) return fused;
   if (a.B <= kFinishMaxBatch && 2 * a.V * s <= kFinishMaxResidualBytes) return ChainPath::kFinish;
+  // Wider rows: chain_finish once it spreads over 64 compute units or more with several
+  // workgroups per sequence (16 <= B <= 128), else the multi-kernel path.  Measured per call
+  // (split / finish): B = 16, gamma = 4, V = 128256 bf16 24.8 / 24.1 us; B = 32 31.7 / 30.3;
+  // B = 64 45.4-46.2 / 43.6; B = 64, gamma = 7 62.4 / 60.0; B = 96 60.2 / 59.7; B = 128 75.5 /
+  // 73.4; B = 64 and 128, gamma = 4, V = 65536 fp32 43.2 / 40.3 and 70.3 / 67.6; but B = 8,
+  // gamma = 7, V = 152064 fp32 29.6 / 32.1 and B = 1 19.0 / 21.2, where the multi-kernel
+  // path's residual pass spreads a sequence over the whole chip.
+  if (a.B >= kFinishGroupsMinBatch && finish_groups(a.B, nchunk) > 1) return ChainPath::kFinish;
   return ChainPath::kSplit;
 }
 

@@ -45,6 +45,7 @@ def kernels_of(batch, monkeypatch, lazy=False, offset=0):
     (1, 4, 1000, "f32", {"chain_fused"}),                  # small rows (the B = 1 fp32 workload)
     (1, 7, 32000, "bf16", {"chain_sweep", "chain_finish"}),  # B = 1, V = 32000: sweep + finish
     (8, 4, 70000, "bf16", SPLIT),                          # wide rows, small batch: split
+    (64, 4, 70000, "bf16", {"chain_sweep", "chain_finish"}),  # wide rows, 16..128: finish
     (200, 2, 20000, "f32", {"chain_fused"}),               # 192..256 sequences fill the chip
     (300, 2, 20000, "bf16", {"chain_sweep", "chain_finish"}),  # B <= 512, narrow residual rows
     (600, 2, 20000, "bf16", SPLIT),                        # past every one-workgroup gate
@@ -67,8 +68,7 @@ def test_unaligned_rows_take_split(monkeypatch):
                             "chain_draw"}),                       # wide pairs: staged
     (192, 3, 65536, "bf16", {"chain_stage", "chain_stage_decide", "chain_residual",
                              "chain_draw"}),                      # 48 MiB of first pairs: staged
-    (128, 3, 40000, "f32", {"chain_sweep", "chain_decide", "chain_residual",
-                            "chain_draw"}),                       # below that: eager (split)
+    (128, 3, 40000, "f32", {"chain_sweep", "chain_finish"}),      # below that: eager (finish)
 ])
 def test_early_exit_form_choice(B, gamma, V, dtype, want, monkeypatch):
     b = I.chain_gaussian(62 + B, B, gamma, V, dtype, 2.0, 1.0, 1.0)
