@@ -27,6 +27,7 @@ CASES = [
     (64, 3, 32768, "bf16"),   # the largest batch with 4 workgroups per sequence
     (100, 2, 32000, "bf16"),  # 2 workgroups per sequence
     (128, 3, 36000, "f32"),   # 18 chunks; the largest batch with 2 workgroups
+    (64, 4, 70000, "bf16"),   # a 273 KiB row pair: finish by the wide-row gate (16..128 sequences)
 ]
 
 
@@ -77,7 +78,24 @@ def test_same_bits_as_one_workgroup_and_oracle(B, gamma, V, dtype, monkeypatch):
             assert np.array_equal(outs[path][k], fin[k], equal_nan=True), (path, k)
 
 
-@pytest.mark.parametrize("B,gamma,V,dtype", [CASES[0], CASES[3]])
+def test_wide_rows_take_finish_unforced(monkeypatch):
+    b = batch(*CASES[5])
+    d = BD.chain_to_device(b)
+    monkeypatch.delenv("SPECVERIFY_CHAIN_PATH", raising=False)
+    torch.cuda.synchronize()
+    BD.trace_start(256)
+    try:
+        out = BD.sv_verify_chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"],
+                                 d["temperature"])
+        torch.cuda.synchronize()
+        names = set(BD.trace_kernels())
+    finally:
+        BD.trace_stop()
+    assert names == {"chain_sweep", "chain_finish"}, names
+    check_chain(b, {k: v.cpu().numpy() for k, v in out.items()})
+
+
+@pytest.mark.parametrize("B,gamma,V,dtype", [CASES[0], CASES[3], CASES[5]])
 def test_with_rates(B, gamma, V, dtype, monkeypatch):
     b = batch(B, gamma, V, dtype)
     d = BD.chain_to_device(b)
